@@ -1,0 +1,276 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) dropless MoE expert-FFN library.
+ *
+ * The layer, for T tokens of width d routed to k of E local experts (R = T*k
+ * routed rows), each expert an FFN of width f:
+ *
+ *   route top-k  ->  permute into expert-contiguous rows  ->  FC1 grouped GEMM
+ *   with a fused GLU epilogue  ->  FC2 grouped GEMM  ->  weighted combine,
+ *
+ * and the backward pass (combine backward, FC2 dgrad with a fused dGLU
+ * epilogue, weight gradients, FC1 dgrad, unpermute-sum, route backward).
+ *
+ * Sources (page title and section):
+ *  [P1] "高度な融合カーネルによる MoE 学習スループットの向上" (NVIDIA developer-blog
+ *       post on fused MoE kernels, Japanese rendering):
+ *       - "MoE ブロックにおけるトレーニングのボトルネック克服": per-expert token
+ *         counts are a run-time quantity; kernel families GroupGemm + Quantize,
+ *         GroupGemm + Activation, GroupGemm + dActivation; SwiGLU, GeGLU and
+ *         sReLU with clamp and scaling options.
+ *       - "融合された GEMM エピローグによる GLU 活性化関数の最適化" (+ Figure 2):
+ *         GLU epilogue on weights repacked into interleaved input/gate column
+ *         tiles; dSwiGLU in the backward epilogue; feature scaling, clamp and
+ *         bias-vector add in the epilogue.
+ *       - "ホストとデバイスの同期および CPU 起動オーバーヘッドの排除": the grouped
+ *         GEMM reads the tokens per group from GPU memory, so no host sync is
+ *         needed and the whole iteration can be graph-captured.
+ *       - "カーネルレベルでの向上から事前学習全体の速度向上へ": dynamic
+ *         scheduling and a configurable limit on the compute units a kernel uses.
+ *  [P2] "JAXとNVIDIA Transformer EngineによるDropless MoE学習の高速化",
+ *       section "主張と根拠": dropless MoE over ragged tensors, one grouped GEMM
+ *       call over all ragged groups.
+ *
+ * Conventions (all entry points):
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees, copies device->host or synchronises.  Each call
+ *    only enqueues kernels on `stream` (a hipStream_t; NULL = default stream),
+ *    so every call may be recorded into a HIP graph.
+ *  - Tensors are dense and row-major.  Sizes known on the host (T, d, f, E, k)
+ *    are ints; the routing-dependent sizes (per-expert counts and offsets)
+ *    exist only in device memory and are read there by the kernels.
+ *  - Weights use the [out, in] convention: W1 [E, n1, d] (n1 = 2f for gated
+ *    activations, f for squared ReLU), W2 [E, d, f].  Biases are float32.
+ *  - Element types: MOE_F32 (float32) or MOE_BF16 (bfloat16, round to nearest
+ *    even on store, float32 accumulation).
+ *  - Alignment: every pointer 16-byte aligned; d and f multiples of 32.
+ *  - Errors: argument errors are returned synchronously as a status code and
+ *    nothing is enqueued.  A failed kernel launch returns MOE_ERR_HIP.  Data
+ *    errors found on the device (NaN logits, expert ids out of range) never
+ *    stop the kernels; they OR bits into the optional device word `err_word`
+ *    (MOE_ERRBIT_*), which the caller may read at any time.
+ *  - Results are deterministic: no floating-point atomics anywhere.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, k > E ... */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented combination */
+  MOE_ERR_WORKSPACE = 3,    /* workspace too small */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_ACT_SWIGLU = 0,  /* silu_a(gate) * lin,  silu_a(g) = g * sigmoid(a g)   */
+  MOE_ACT_GEGLU = 1,   /* gelu(gate) * lin (erf form; tanh form by flag)        */
+  MOE_ACT_SRELU = 2    /* relu(h)^2, not gated: FC1 has n1 = f output columns   */
+} moe_act_t;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_t;
+
+typedef enum { MOE_BWD_DGRAD = 0, MOE_BWD_WGRAD = 1 } moe_bwd_mode_t;
+
+#define MOE_ERRBIT_NAN_LOGIT 1u    /* a router logit was NaN (ranked as -inf)   */
+#define MOE_ERRBIT_BAD_EXPERT 2u   /* an expert id outside [0, E) (counted as 0) */
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/* Library version string and readable status names. */
+const char* moe_version(void);
+const char* moe_status_string(moe_status_t s);
+
+/* Rows per repack chunk G of the packed FC1 weight layout (see
+ * moe_repack_glu_weights).  f must be a multiple of G. */
+int moe_glu_granularity(void);
+
+/* ---------------------------------------------------------------- routing
+ * a1.  Top-k routing [P1 "MoE ブロックにおけるトレーニングのボトルネック克服"].
+ *   logits   [T, E] float32 (in)
+ *   topk_idx [T, k] int32 (out): the k experts with the largest logits,
+ *            largest first; equal logits are taken in increasing expert id;
+ *            NaN logits rank as -inf and set MOE_ERRBIT_NAN_LOGIT.
+ *   topk_w   [T, k] float32 (out): gate weights.  SOFTMAX: softmax over the
+ *            selected logits when `normalize` (= full softmax renormalised
+ *            over the selection), else the full-softmax probabilities.
+ *            SIGMOID: sigmoid(l) / sum over the selection when `normalize`,
+ *            else sigmoid(l).
+ *   err_word int32 device word (in/out, nullable).
+ * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS. */
+moe_status_t moe_route_topk(const float* logits, int T, int E, int k, int score, int normalize,
+                            int32_t* topk_idx, float* topk_w, int32_t* err_word, void* stream);
+
+/* a7.  Gradient of the gate weights with respect to the logits.
+ *   d_topk_w [T, k] float32 (in): dLoss/dtopk_w;  d_logits [T, E] float32
+ *   (out, fully overwritten; 0 for unselected experts except for the
+ *   unnormalised softmax, whose denominator involves every logit). */
+moe_status_t moe_route_topk_bwd(const float* logits, const int32_t* topk_idx,
+                                const float* d_topk_w, int T, int E, int k, int score,
+                                int normalize, float* d_logits, void* stream);
+
+/* ---------------------------------------------------------------- permute
+ * a2.  Expert-contiguous layout [P2 "主張と根拠"; P1 "ホストとデバイスの同期…"].
+ * The row of assignment i = t*k + j (expert e) is
+ *     offsets[e] + #{ i' < i : expert(i') = e }
+ * (a stable counting sort by expert).
+ *   x          [T, d] dtype (in); may be NULL when xp is NULL.
+ *   topk_idx   [T, k] int32 (in)
+ *   counts     [E] int32 (out), offsets [E+1] int32 (out, exclusive scan,
+ *              offsets[E] = T*k), pad_offsets [E+1] int32 (out, nullable:
+ *              offsets of the segments padded to multiples of 32 rows)
+ *   row_map    [T, k] int32 (out): row of each assignment
+ *   src_row    [T*k] int32 (out): token of each row
+ *   xp         [T*k, d] dtype (out, nullable): xp[r] = x[src_row[r]]
+ *   ws         device workspace of at least moe_permute_workspace_size() bytes
+ * Ids outside [0, E) set MOE_ERRBIT_BAD_EXPERT and are counted as expert 0,
+ * so the outputs always form a valid permutation. */
+size_t moe_permute_workspace_size(int T, int E, int k);
+moe_status_t moe_permute(const void* x, int dtype, int T, int d, const int32_t* topk_idx,
+                         int k, int E, int32_t* counts, int32_t* offsets,
+                         int32_t* pad_offsets, int32_t* row_map, int32_t* src_row, void* xp,
+                         void* ws, size_t ws_bytes, int32_t* err_word, void* stream);
+
+/* ---------------------------------------------------------------- repack
+ * a13.  FC1 weight repack [P1 "融合された GEMM エピローグ…", Figure 2].
+ * Canonical W1 rows [0, f) are the gate chunk (activated) and [f, 2f) the
+ * linear chunk.  The packed layout alternates G-row chunks (G =
+ * moe_glu_granularity()): gate chunk c -> packed rows [2Gc, 2Gc+G), linear
+ * chunk c -> [2Gc+G, 2Gc+2G), so every 2G-wide output tile of FC1 holds the
+ * matching gate and linear columns.  A bit-exact row permutation.
+ *   w   [E, 2f, d] dtype (in), b [E, 2f] float32 (in, nullable)
+ *   w_out, b_out: same shapes (out; b_out nullable iff b is); must not alias
+ *   inverse = 1 maps packed -> canonical (for exporting dW1 / db1). */
+moe_status_t moe_repack_glu_weights(const void* w, const float* b, int dtype, int E, int f,
+                                    int d, int inverse, void* w_out, float* b_out,
+                                    void* stream);
+
+/* ---------------------------------------------------------------- grouped GEMMs
+ * All grouped GEMMs run over the expert segments given by the DEVICE array
+ * offsets [E+1] (offsets[0] = 0, nondecreasing, offsets[E] = R); segment e
+ * holds rows [offsets[e], offsets[e+1]).  One persistent launch covers every
+ * expert: its workgroups read the offsets and enumerate their tiles on the
+ * device.  `max_cus` > 0 limits the compute units the launch occupies
+ * (0 = all) [P1 "カーネルレベルでの向上…": configurable margin]. */
+
+/* a3.  FC1 with the GLU epilogue [P1 "融合された GEMM エピローグ…"]:
+ *   H[r]  = xp[r] @ w1p[e]^T + b1p[e]            (float32 accumulate)
+ *   A[r]  = act(gate cols of H, linear cols of H) (see moe_act_t)
+ * with optional clamp: gate <- min(gate, L), lin <- clip(lin, -L, L) when
+ * clamp > 0 (for SRELU: h <- min(h, L)).
+ *   xp  [R, d] dtype;  w1p [E, n1, d] dtype, packed (gated acts);
+ *   b1p [E, n1] float32 nullable (packed like w1p);
+ *   h_out [R, n1] dtype nullable: pre-activation H saved for the backward;
+ *   a_out [R, f] dtype.
+ * alpha: slope of SwiGLU's sigmoid (1 = SiLU); gelu_tanh selects GeGLU's
+ * tanh form. */
+typedef struct {
+  size_t struct_size; /* = sizeof(moe_glu_fwd_args_t) */
+  int dtype;
+  const void* xp;
+  const void* w1p;
+  const float* b1p;
+  const int32_t* offsets;
+  int E, R, d, f;
+  int act;
+  float clamp;
+  float alpha;
+  int gelu_tanh;
+  void* h_out;
+  void* a_out;
+  int max_cus;
+} moe_glu_fwd_args_t;
+moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* args, void* stream);
+
+/* a4.  Plain grouped GEMM ("linear"): y[r] = a[r] @ w[e]^T + b[e]
+ *   a [R, K] dtype;  w [E, N, K] dtype;  b [E, N] float32 nullable;
+ *   y [R, N] dtype.  (FC2: K = f, N = d.) */
+typedef struct {
+  size_t struct_size; /* = sizeof(moe_gemm_fwd_args_t) */
+  int dtype;
+  const void* a;
+  const void* w;
+  const float* b;
+  const int32_t* offsets;
+  int E, R, N, K;
+  void* y;
+  int max_cus;
+} moe_gemm_fwd_args_t;
+moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* args, void* stream);
+
+/* a8.  FC2 dgrad with the dGLU epilogue [P1 "融合された GEMM エピローグ…":
+ * the backward epilogue reads the GEMM output and computes dSwiGLU]:
+ *   dA[r] = dy[r] @ w2[e]                        (float32 accumulate)
+ *   dH    = (dA * lin * act'(gate) * [gate <= L],  dA * act(gate) * [|lin| <= L])
+ * written in the packed column layout of h (for SRELU: dH = dA * 2 relu(h) * [h <= L]).
+ *   dy [R, d] dtype;  w2 [E, d, f] dtype;  h [R, n1] dtype (saved by FC1);
+ *   dh [R, n1] dtype (out). */
+typedef struct {
+  size_t struct_size; /* = sizeof(moe_glu_bwd_args_t) */
+  int dtype;
+  const void* dy;
+  const void* w2;
+  const void* h;
+  const int32_t* offsets;
+  int E, R, d, f;
+  int act;
+  float clamp;
+  float alpha;
+  int gelu_tanh;
+  void* dh;
+  int max_cus;
+} moe_glu_bwd_args_t;
+moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* args, void* stream);
+
+/* a9 / a10 / a11.  Backward of the grouped linear map y = a @ w[e]^T (+ b[e]):
+ *   DGRAD: da[r] = g[r] @ w[e]                 g [R, N], w [E, N, K] dtype,
+ *          da [R, K] dtype (out).
+ *   WGRAD: dw[e] = g[seg e]^T @ a[seg e]       g [R, N], a [R, K] dtype,
+ *          dw [E, N, K] float32 (out; exact zeros for empty experts; added to
+ *          the existing values when `accumulate`), db [E, N] float32
+ *          (out, nullable): column sums of g over each segment. */
+typedef struct {
+  size_t struct_size; /* = sizeof(moe_gemm_bwd_args_t) */
+  int dtype;
+  int mode;            /* moe_bwd_mode_t */
+  const void* g;
+  const void* a;       /* WGRAD */
+  const void* w;       /* DGRAD */
+  const int32_t* offsets;
+  int E, R, N, K;
+  void* out;           /* da (DGRAD) or dw (WGRAD) */
+  float* db;           /* WGRAD, nullable */
+  int accumulate;
+  int max_cus;
+} moe_gemm_bwd_args_t;
+moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream);
+
+/* ---------------------------------------------------------------- combine
+ * a5 / a12.  out[t] = sum_{j=0..k-1} topk_w[t,j] * y[row_map[t,j]], summed in
+ * float32 in slot order (topk_w NULL: unit weights, the unpermute-sum of the
+ * backward).  y [T*k, d] dtype; out [T, d] dtype. */
+moe_status_t moe_unpermute_combine(const void* y, int dtype, const int32_t* row_map,
+                                   const float* topk_w, int T, int k, int d, void* out,
+                                   void* stream);
+
+/* a6.  Backward of the combine:
+ *   d_y[row_map[t,j]]  = topk_w[t,j] * d_out[t]        (dtype, rounded once)
+ *   d_topk_w[t,j]      = <d_out[t], y[row_map[t,j]]>   (float32)
+ * d_out [T, d], y [T*k, d], d_y [T*k, d] dtype. */
+moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dtype,
+                                       const int32_t* row_map, const float* topk_w, int T,
+                                       int k, int d, void* d_y, float* d_topk_w, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -547,7 +547,7 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
     dXp_s = rnd(dXp)
     dX = combine(dXp_s, row_map, None)
     out = dict(dY=dY_s, dgate=dgate, dlogits=dlogits, dA=dA, dH=dH_s, dW2=dW2, dXp=dXp_s,
-               dW1=dW1, dX=rnd(dX))
+               dW1=dW1, dX=rnd(dX), dY_exact=dY, dH_exact=dH, dXp_exact=dXp, dX_exact=dX)
     if has_bias:
         out["db1"] = db1
         out["db2"] = db2

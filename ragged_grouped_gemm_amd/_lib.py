@@ -1,0 +1,114 @@
+"""ctypes loader of ``libmoe_mi355x.so`` and the C structures of ``include/moe.h``.
+
+The library is built in-tree by ``python -m ragged_grouped_gemm_amd.build``.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+ACT = {"swiglu": 0, "geglu": 1, "srelu": 2}
+SCORE = {"softmax": 0, "sigmoid": 1}
+MOE_BWD_DGRAD, MOE_BWD_WGRAD = 0, 1
+ERRBIT_NAN_LOGIT, ERRBIT_BAD_EXPERT = 1, 2
+
+c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class GluFwdArgs(ctypes.Structure):
+    _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("xp", c_void_p), ("w1p", c_void_p),
+                ("b1p", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
+                ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
+                ("alpha", c_float), ("gelu_tanh", c_int), ("h_out", c_void_p),
+                ("a_out", c_void_p), ("max_cus", c_int)]
+
+
+class GemmFwdArgs(ctypes.Structure):
+    _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("a", c_void_p), ("w", c_void_p),
+                ("b", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
+                ("N", c_int), ("K", c_int), ("y", c_void_p), ("max_cus", c_int)]
+
+
+class GluBwdArgs(ctypes.Structure):
+    _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("dy", c_void_p), ("w2", c_void_p),
+                ("h", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
+                ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
+                ("alpha", c_float), ("gelu_tanh", c_int), ("dh", c_void_p),
+                ("max_cus", c_int)]
+
+
+class GemmBwdArgs(ctypes.Structure):
+    _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("mode", c_int), ("g", c_void_p),
+                ("a", c_void_p), ("w", c_void_p), ("offsets", c_void_p), ("E", c_int),
+                ("R", c_int), ("N", c_int), ("K", c_int), ("out", c_void_p), ("db", c_void_p),
+                ("accumulate", c_int), ("max_cus", c_int)]
+
+
+_SIGS = {
+    "moe_version": (ctypes.c_char_p, []),
+    "moe_status_string": (ctypes.c_char_p, [c_int]),
+    "moe_glu_granularity": (c_int, []),
+    "moe_route_topk": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                               c_void_p, c_void_p]),
+    "moe_route_topk_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                   c_int, c_void_p, c_void_p]),
+    "moe_permute_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "moe_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p,
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                            c_void_p, c_void_p]),
+    "moe_repack_glu_weights": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                       c_void_p, c_void_p, c_void_p]),
+    "moe_grouped_gemm_glu_fwd": (c_int, [ctypes.POINTER(GluFwdArgs), c_void_p]),
+    "moe_grouped_gemm_fwd": (c_int, [ctypes.POINTER(GemmFwdArgs), c_void_p]),
+    "moe_grouped_gemm_glu_bwd": (c_int, [ctypes.POINTER(GluBwdArgs), c_void_p]),
+    "moe_grouped_gemm_bwd": (c_int, [ctypes.POINTER(GemmBwdArgs), c_void_p]),
+    "moe_unpermute_combine": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                      c_void_p, c_void_p]),
+    "moe_unpermute_combine_bwd": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int,
+                                          c_int, c_int, c_void_p, c_void_p, c_void_p]),
+}
+
+_lib = None
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions declared in the C header."""
+    with open(path) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def load():
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m ragged_grouped_gemm_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def check(status: int, what: str):
+    if status != MOE_OK:
+        name = load().moe_status_string(status).decode()
+        raise MoEError(f"{what} failed: {name} ({status})")

@@ -1,0 +1,210 @@
+// Weighted unpermute / combine and its backward.
+//
+// out[t] = sum_{j<k} w[t,j] * y[row_map[t,j]]: the gate-weighted sum of a
+// token's k expert outputs, accumulated in float32 in slot order and rounded
+// once.  The backward scatters w[t,j] * dout[t] to the rows and takes the dot
+// products <dout[t], y[row]> for the gate gradient.  Both are HBM-bound
+// gathers: one wave per token, 16-byte vectors along d, no atomics (each row
+// belongs to exactly one (t, j)), so results are deterministic.
+#include "common.hpp"
+
+namespace moe {
+
+template <class EL>
+__global__ void __launch_bounds__(256) combine_kernel(const u32x4* __restrict__ y,
+                                                      const int32_t* __restrict__ row_map,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int R, int chunks, u32x4* __restrict__ out) {
+  constexpr int V = EL::VEC;
+  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int lane = threadIdx.x & 63;
+  int rows[MOE_MAX_TOPK];
+  float ws[MOE_MAX_TOPK];
+  for (int j = 0; j < k; ++j) {
+    int r = row_map[(size_t)t * k + j];
+    rows[j] = (r < 0 || r >= R) ? 0 : r;
+    ws[j] = w ? w[(size_t)t * k + j] : 1.0f;
+  }
+  for (int c = lane; c < chunks; c += 64) {
+    float acc[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      float v[V];
+      unpack_chunk(y[(size_t)rows[j] * chunks + c], v, EL());
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = fmaf(ws[j], v[q], acc[q]);
+    }
+    out[(size_t)t * chunks + c] = pack_chunk(acc, EL());
+  }
+}
+
+template <class EL>
+__global__ void __launch_bounds__(256) combine_bwd_kernel(
+    const u32x4* __restrict__ dout, const u32x4* __restrict__ y,
+    const int32_t* __restrict__ row_map, const float* __restrict__ w, int T, int k, int R,
+    int chunks, u32x4* __restrict__ dy, float* __restrict__ dw) {
+  constexpr int V = EL::VEC;
+  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int lane = threadIdx.x & 63;
+  for (int j = 0; j < k; ++j) {
+    int r = row_map[(size_t)t * k + j];
+    r = (r < 0 || r >= R) ? 0 : r;
+    float wj = w[(size_t)t * k + j];
+    float part = 0.0f;
+    for (int c = lane; c < chunks; c += 64) {
+      float g[V], v[V], o[V];
+      unpack_chunk(dout[(size_t)t * chunks + c], g, EL());
+      unpack_chunk(y[(size_t)r * chunks + c], v, EL());
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        part = fmaf(g[q], v[q], part);
+        o[q] = wj * g[q];
+      }
+      dy[(size_t)r * chunks + c] = pack_chunk(o, EL());
+    }
+    float tot = wave_sum(part);
+    if (lane == 0 && dw) dw[(size_t)t * k + j] = tot;
+  }
+}
+
+// Bias gradient of a grouped linear map: db[e][n] = sum over the rows of
+// segment e of g[r][n], float32, rows summed in order (deterministic).
+// grid: (ceil(N / 256), E); each thread owns one column.
+template <class EL>
+__global__ void __launch_bounds__(256) segment_colsum_kernel(const typename EL::storage* g,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int R, int N, float* db) {
+  int n = blockIdx.x * 256 + threadIdx.x;
+  int e = blockIdx.y;
+  if (n >= N) return;
+  int s = min(max(offsets[e], 0), R), t = min(max(offsets[e + 1], 0), R);
+  float acc = 0.0f;
+  for (int r = s; r < t; ++r) {
+    float v;
+    if constexpr (EL::VEC == 8)
+      v = bf16_bits_to_f32(g[(size_t)r * N + n]);
+    else
+      v = g[(size_t)r * N + n];
+    acc += v;
+  }
+  db[(size_t)e * N + n] = acc;
+}
+
+template __global__ void segment_colsum_kernel<BF16>(const uint16_t*, const int32_t*, int, int,
+                                                     float*);
+template __global__ void segment_colsum_kernel<F32>(const float*, const int32_t*, int, int, float*);
+
+moe_status_t launch_segment_colsum(int dtype, const void* g, const int32_t* offsets, int E,
+                                   int R, int N, float* db, hipStream_t s) {
+  dim3 grid((N + 255) / 256, E);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(segment_colsum_kernel<BF16>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(g), offsets, R, N, db);
+  else
+    hipLaunchKernelGGL(segment_colsum_kernel<F32>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const float*>(g), offsets, R, N, db);
+  return launch_status();
+}
+
+// Row permutation of the FC1 weights between canonical and packed layouts.
+// Canonical row i < f (gate) <-> packed 2G*(i/G) + i%G; row f+i (linear) <->
+// packed 2G*(i/G) + G + i%G.  One wave per row; 16-byte copies.
+__device__ __forceinline__ int packed_row(int i, int f, int G) {
+  if (i < f) return 2 * G * (i / G) + i % G;
+  i -= f;
+  return 2 * G * (i / G) + G + i % G;
+}
+
+__global__ void __launch_bounds__(256) repack_kernel(const u32x4* __restrict__ w,
+                                                     const float* __restrict__ b, int E, int f,
+                                                     int G, int chunks, int inverse,
+                                                     u32x4* __restrict__ wo,
+                                                     float* __restrict__ bo) {
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // global row over E * 2f
+  int lane = threadIdx.x & 63;
+  if (row >= E * 2 * f) return;
+  int e = row / (2 * f), i = row % (2 * f);
+  int p = packed_row(i, f, G);
+  int src = inverse ? p : i, dst = inverse ? i : p;
+  const u32x4* s = w + ((size_t)e * 2 * f + src) * chunks;
+  u32x4* d = wo + ((size_t)e * 2 * f + dst) * chunks;
+  for (int c = lane; c < chunks; c += 64) d[c] = s[c];
+  if (b && lane == 0) bo[(size_t)e * 2 * f + dst] = b[(size_t)e * 2 * f + src];
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_glu_granularity(void) { return 32; }
+
+moe_status_t moe_unpermute_combine(const void* y, int dtype, const int32_t* row_map,
+                                   const float* topk_w, int T, int k, int d, void* out,
+                                   void* stream) {
+  MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && d > 0 && valid_dtype(dtype));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(y && row_map && out && aligned16(y) && aligned16(out));
+  MOE_CHECK_ARG((d * dtype_size(dtype)) % 16 == 0);
+  int chunks = (int)(d * dtype_size(dtype) / 16);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<BF16>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const u32x4*>(y), row_map, topk_w, T, k, T * k, chunks,
+                       reinterpret_cast<u32x4*>(out));
+  else
+    hipLaunchKernelGGL(combine_kernel<F32>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const u32x4*>(y), row_map, topk_w, T, k, T * k, chunks,
+                       reinterpret_cast<u32x4*>(out));
+  return launch_status();
+}
+
+moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dtype,
+                                       const int32_t* row_map, const float* topk_w, int T,
+                                       int k, int d, void* d_y, float* d_topk_w, void* stream) {
+  MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && d > 0 && valid_dtype(dtype));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(d_out && y && row_map && topk_w && d_y);
+  MOE_CHECK_ARG(aligned16(d_out) && aligned16(y) && aligned16(d_y));
+  MOE_CHECK_ARG((d * dtype_size(dtype)) % 16 == 0);
+  int chunks = (int)(d * dtype_size(dtype) / 16);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<BF16>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const u32x4*>(d_out), reinterpret_cast<const u32x4*>(y),
+                       row_map, topk_w, T, k, T * k, chunks, reinterpret_cast<u32x4*>(d_y),
+                       d_topk_w);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<F32>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const u32x4*>(d_out), reinterpret_cast<const u32x4*>(y),
+                       row_map, topk_w, T, k, T * k, chunks, reinterpret_cast<u32x4*>(d_y),
+                       d_topk_w);
+  return launch_status();
+}
+
+moe_status_t moe_repack_glu_weights(const void* w, const float* b, int dtype, int E, int f,
+                                    int d, int inverse, void* w_out, float* b_out,
+                                    void* stream) {
+  const int G = moe_glu_granularity();
+  MOE_CHECK_ARG(E >= 1 && f > 0 && d > 0 && valid_dtype(dtype) && f % G == 0);
+  MOE_CHECK_ARG(w && w_out && w != w_out && aligned16(w) && aligned16(w_out));
+  MOE_CHECK_ARG((b == nullptr) == (b_out == nullptr));
+  MOE_CHECK_ARG(b == nullptr || (const void*)b != (const void*)b_out);
+  MOE_CHECK_ARG((d * dtype_size(dtype)) % 16 == 0);
+  int chunks = (int)(d * dtype_size(dtype) / 16);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  size_t rows = (size_t)E * 2 * f;
+  MOE_CHECK_ARG(rows < (size_t)INT32_MAX);
+  hipLaunchKernelGGL(repack_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4*>(w), b, E, f, G, chunks, inverse,
+                     reinterpret_cast<u32x4*>(w_out), b_out);
+  return launch_status();
+}
+
+}  // extern "C"

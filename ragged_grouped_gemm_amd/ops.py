@@ -1,0 +1,208 @@
+"""Python binding of the C ABI: one function per entry point, same names.
+
+Arguments are torch tensors on the GPU; the functions only check shapes,
+marshal pointers and the current stream, and call the library.  Every step of
+the computation runs in the library's HIP kernels.  Output tensors may be
+passed in (preallocated, e.g. for graph capture) or are allocated here.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import ACT, SCORE, check
+
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def moe_version() -> str:
+    return _lib.load().moe_version().decode()
+
+
+def moe_glu_granularity() -> int:
+    return _lib.load().moe_glu_granularity()
+
+
+def moe_route_topk(logits, k, score="softmax", normalize=True, topk_idx=None, topk_w=None,
+                   err_word=None):
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    topk_idx = _empty((T, k), torch.int32, logits) if topk_idx is None else topk_idx
+    topk_w = _empty((T, k), torch.float32, logits) if topk_w is None else topk_w
+    check(_lib.load().moe_route_topk(_p(logits), T, E, k, SCORE[score], int(normalize),
+                                     _p(topk_idx), _p(topk_w), _p(err_word), _stream()),
+          "moe_route_topk")
+    return topk_idx, topk_w
+
+
+def moe_route_topk_bwd(logits, topk_idx, d_topk_w, score="softmax", normalize=True,
+                       d_logits=None):
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    d_logits = _empty((T, E), torch.float32, logits) if d_logits is None else d_logits
+    check(_lib.load().moe_route_topk_bwd(_p(logits), _p(topk_idx), _p(d_topk_w), T, E, k,
+                                         SCORE[score], int(normalize), _p(d_logits), _stream()),
+          "moe_route_topk_bwd")
+    return d_logits
+
+
+def moe_permute_workspace_size(T, E, k) -> int:
+    return int(_lib.load().moe_permute_workspace_size(T, E, k))
+
+
+def moe_permute(x, topk_idx, E, *, counts=None, offsets=None, pad_offsets=None, row_map=None,
+                src_row=None, xp=None, ws=None, err_word=None, gather=True, want_pad=False):
+    """Returns (counts, offsets, pad_offsets, row_map, src_row, xp)."""
+    T, k = topk_idx.shape
+    dev = topk_idx
+    counts = _empty((E,), torch.int32, dev) if counts is None else counts
+    offsets = _empty((E + 1,), torch.int32, dev) if offsets is None else offsets
+    if want_pad and pad_offsets is None:
+        pad_offsets = _empty((E + 1,), torch.int32, dev)
+    row_map = _empty((T, k), torch.int32, dev) if row_map is None else row_map
+    src_row = _empty((T * k,), torch.int32, dev) if src_row is None else src_row
+    d = 0
+    dt = _lib.MOE_BF16
+    if gather:
+        d = x.shape[1]
+        dt = _dtype(x)
+        xp = _empty((T * k, d), x.dtype, x) if xp is None else xp
+    else:
+        xp = None
+    nbytes = moe_permute_workspace_size(T, E, k)
+    if ws is None:
+        ws = _empty((nbytes,), torch.uint8, dev)
+    check(_lib.load().moe_permute(_p(x) if gather else None, dt, T, d, _p(topk_idx), k, E,
+                                  _p(counts), _p(offsets), _p(pad_offsets), _p(row_map),
+                                  _p(src_row), _p(xp), _p(ws), ws.numel() * ws.element_size(),
+                                  _p(err_word), _stream()),
+          "moe_permute")
+    return counts, offsets, pad_offsets, row_map, src_row, xp
+
+
+def moe_repack_glu_weights(w, b=None, inverse=False, w_out=None, b_out=None):
+    E, n1, d = w.shape
+    f = n1 // 2
+    w_out = torch.empty_like(w) if w_out is None else w_out
+    if b is not None and b_out is None:
+        b_out = torch.empty_like(b)
+    check(_lib.load().moe_repack_glu_weights(_p(w), _p(b), _dtype(w), E, f, d, int(inverse),
+                                             _p(w_out), _p(b_out), _stream()),
+          "moe_repack_glu_weights")
+    return w_out, b_out
+
+
+def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=0.0, alpha=1.0,
+                             gelu_tanh=False, save_h=True, h_out=None, a_out=None, max_cus=0):
+    """FC1 + GLU epilogue.  Returns (A [R, f], H [R, n1] or None)."""
+    R, d = xp.shape
+    E, n1, _ = w1p.shape
+    f = n1 if act == "srelu" else n1 // 2
+    a_out = _empty((R, f), xp.dtype, xp) if a_out is None else a_out
+    if save_h and h_out is None:
+        h_out = _empty((R, n1), xp.dtype, xp)
+    args = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _dtype(xp), _p(xp), _p(w1p), _p(b1p),
+                           _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
+                           _p(h_out) if save_h else None, _p(a_out), max_cus)
+    check(_lib.load().moe_grouped_gemm_glu_fwd(ctypes.byref(args), _stream()),
+          "moe_grouped_gemm_glu_fwd")
+    return a_out, (h_out if save_h else None)
+
+
+def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0):
+    """y[r] = a[r] @ w[e]^T (+ b[e])."""
+    R, K = a.shape
+    E, N, _ = w.shape
+    y = _empty((R, N), a.dtype, a) if y is None else y
+    args = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), _dtype(a), _p(a), _p(w), _p(b),
+                            _p(offsets), E, R, N, K, _p(y), max_cus)
+    check(_lib.load().moe_grouped_gemm_fwd(ctypes.byref(args), _stream()), "moe_grouped_gemm_fwd")
+    return y
+
+
+def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alpha=1.0,
+                             gelu_tanh=False, dh=None, max_cus=0):
+    """FC2 dgrad + dGLU epilogue -> dH [R, n1] (packed like h)."""
+    R, d = dy.shape
+    E, _, f = w2.shape
+    dh = torch.empty_like(h) if dh is None else dh
+    args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), _dtype(dy), _p(dy), _p(w2), _p(h),
+                           _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
+                           _p(dh), max_cus)
+    check(_lib.load().moe_grouped_gemm_glu_bwd(ctypes.byref(args), _stream()),
+          "moe_grouped_gemm_glu_bwd")
+    return dh
+
+
+def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None, want_db=False,
+                         accumulate=False, max_cus=0):
+    """mode "dgrad": da = g @ w[e];  mode "wgrad": dw[e] = g[seg]^T @ a[seg] (+ db)."""
+    R, N = g.shape
+    if mode == "dgrad":
+        E, _, K = w.shape
+        out = _empty((R, K), g.dtype, g) if out is None else out
+        m = _lib.MOE_BWD_DGRAD
+    elif mode == "wgrad":
+        K = a.shape[1]
+        E = offsets.shape[0] - 1
+        out = _empty((E, N, K), torch.float32, g) if out is None else out
+        if want_db and db is None:
+            db = _empty((E, N), torch.float32, g)
+        m = _lib.MOE_BWD_WGRAD
+    else:
+        raise ValueError(mode)
+    args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _dtype(g), m, _p(g), _p(a), _p(w),
+                            _p(offsets), E, R, N, K, _p(out), _p(db), int(accumulate), max_cus)
+    check(_lib.load().moe_grouped_gemm_bwd(ctypes.byref(args), _stream()),
+          "moe_grouped_gemm_bwd")
+    return (out, db) if mode == "wgrad" else out
+
+
+def moe_unpermute_combine(y, row_map, topk_w=None, out=None):
+    T, k = row_map.shape
+    d = y.shape[1]
+    out = _empty((T, d), y.dtype, y) if out is None else out
+    check(_lib.load().moe_unpermute_combine(_p(y), _dtype(y), _p(row_map), _p(topk_w), T, k, d,
+                                            _p(out), _stream()),
+          "moe_unpermute_combine")
+    return out
+
+
+def moe_unpermute_combine_bwd(d_out, y, row_map, topk_w, d_y=None, d_topk_w=None):
+    T, k = row_map.shape
+    d = y.shape[1]
+    d_y = torch.empty_like(y) if d_y is None else d_y
+    d_topk_w = _empty((T, k), torch.float32, y) if d_topk_w is None else d_topk_w
+    check(_lib.load().moe_unpermute_combine_bwd(_p(d_out), _p(y), _dtype(y), _p(row_map),
+                                                _p(topk_w), T, k, d, _p(d_y), _p(d_topk_w),
+                                                _stream()),
+          "moe_unpermute_combine_bwd")
+    return d_y, d_topk_w

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function the header declares, and rejects bad arguments with status
+codes before touching the device."""
+import ctypes
+
+import pytest
+
+from ragged_grouped_gemm_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_header_function(lib):
+    names = _lib.header_functions()
+    assert len(names) >= 14
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding declares a signature for each of them
+    assert sorted(_lib._SIGS) == names
+
+
+def test_host_only_queries(lib):
+    assert b"gfx950" in lib.moe_version()
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(4) == b"MOE_ERR_HIP"
+    assert lib.moe_glu_granularity() == 32
+    assert lib.moe_permute_workspace_size(16384, 32, 8) >= 128 * 32 * 4
+    assert lib.moe_permute_workspace_size(16384, 32, 8) % 256 == 0
+
+
+def test_bad_arguments_rejected(lib):
+    INV = _lib.MOE_ERR_INVALID_ARG
+    # k > E, E out of range, null pointers, bad score
+    assert lib.moe_route_topk(None, 4, 2, 3, 0, 1, None, None, None, None) == INV
+    assert lib.moe_route_topk(None, 4, 0, 1, 0, 1, None, None, None, None) == INV
+    assert lib.moe_route_topk(None, 4, 8, 2, 0, 1, None, None, None, None) == INV
+    assert lib.moe_route_topk(None, 4, 8, 2, 7, 1, None, None, None, None) == INV
+    assert lib.moe_route_topk(None, 0, 8, 2, 0, 1, None, None, None, None) == _lib.MOE_OK
+    assert lib.moe_unpermute_combine(None, 1, None, None, 4, 2, 64, None, None) == INV
+    assert lib.moe_unpermute_combine(None, 9, None, None, 4, 2, 64, None, None) == INV
+    # f not a multiple of the repack granularity
+    assert lib.moe_repack_glu_weights(None, None, 1, 2, 48, 64, 0, None, None, None) == INV
+    # too-small permute workspace
+    fake = ctypes.c_void_p(256)
+    st = lib.moe_permute(None, 1, 1000, 0, fake, 2, 8, fake, fake, None, fake, fake, None,
+                         fake, 4, None, None)
+    assert st == _lib.MOE_ERR_WORKSPACE
+    # misaligned pointer
+    a = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), 1, 258, 256, None, 256, 4, 64, 64, 64,
+                         256, 0)
+    assert lib.moe_grouped_gemm_fwd(ctypes.byref(a), None) == INV
+    # struct_size too small (ABI versioning)
+    a = _lib.GemmFwdArgs(8, 1, 256, 256, None, 256, 4, 64, 64, 64, 256, 0)
+    assert lib.moe_grouped_gemm_fwd(ctypes.byref(a), None) == INV
+    # d not a multiple of 32
+    g = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), 1, 256, 256, None, 256, 4, 64, 48, 64, 0,
+                        0.0, 1.0, 0, None, 256, 0)
+    assert lib.moe_grouped_gemm_glu_fwd(ctypes.byref(g), None) == INV
+    b = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), 1, 5, 256, 256, 256, 256, 4, 64, 64, 64,
+                         256, None, 0, 0)
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Field offsets and sizes of the ctypes structures equal the C compiler's."""
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"moe_glu_fwd_args_t": _lib.GluFwdArgs, "moe_gemm_fwd_args_t": _lib.GemmFwdArgs,
+               "moe_glu_bwd_args_t": _lib.GluBwdArgs, "moe_gemm_bwd_args_t": _lib.GemmBwdArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0;}")
+    src = tmp_path / "probe.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    inc = os.path.dirname(_lib.HEADER)
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    got = {}
+    for line in out.splitlines():
+        c, f, v = line.split()
+        got[(c, f)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
