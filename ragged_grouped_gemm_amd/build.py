@@ -51,6 +51,13 @@ def build(jobs: int = 8, debug: bool = False, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A kernel whose host-side stub the compiler failed to emit shows up only as
+    # an undefined symbol; refuse such a library instead of failing at load time.
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.strip() for l in nm.stdout.splitlines() if "moe::" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("library has undefined internal symbols:\n" + "\n".join(missing[:20]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")

@@ -39,10 +39,25 @@
 #include "common.hpp"
 
 #include <math.h>
+#include <stdlib.h>
+
+#include <type_traits>
 
 namespace moe {
 
-enum { EPI_STORE = 0, EPI_GLU_FWD = 1, EPI_GLU_BWD = 2, EPI_SRELU_FWD = 3, EPI_SRELU_BWD = 4 };
+// Epilogues.  The activation is part of the id, so each kernel carries the
+// code of one activation only.
+enum {
+  EPI_STORE = 0,       // C = acc (+ bias)                     (plain grouped GEMM / dgrad / wgrad)
+  EPI_SWIGLU_FWD = 1,  // H = acc + b1;  A = silu_a(gate) * lin (FC1)
+  EPI_GEGLU_FWD = 2,   // H = acc + b1;  A = gelu(gate) * lin   (FC1)
+  EPI_SRELU_FWD = 3,   // H = acc + b1;  A = relu(h)^2          (FC1, not gated)
+  EPI_SWIGLU_BWD = 4,  // dH from dA = acc and the saved H       (FC2 dgrad)
+  EPI_GEGLU_BWD = 5,
+  EPI_SRELU_BWD = 6
+};
+constexpr bool epi_glu_fwd(int e) { return e == EPI_SWIGLU_FWD || e == EPI_GEGLU_FWD; }
+constexpr bool epi_glu_bwd(int e) { return e == EPI_SWIGLU_BWD || e == EPI_GEGLU_BWD; }
 enum { RAGGED_M = 0, RAGGED_K = 1 };
 
 struct GemmArgs {
@@ -65,135 +80,223 @@ struct GemmArgs {
 
 // ------------------------------------------------------------------ activations
 
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)) with the hardware exp2 and reciprocal
+// (relative error about 1e-6 for |x| <= 20; exact limits 0 and 1 outside).
+__device__ __forceinline__ float sigm(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
 
-__device__ __forceinline__ float act_fwd(float g, int act, float alpha, int gtanh) {
-  if (act == MOE_ACT_SWIGLU) return g * sigm(alpha * g);
-  if (act == MOE_ACT_GEGLU) {
+// Activation value and derivative.  GATED_SWIGLU: silu_a(g) = g sigmoid(a g);
+// GATED_GEGLU: g Phi(g) (erf form) or its tanh approximation; SRELU: relu(g)^2.
+enum { ACT_SWIGLU = 0, ACT_GEGLU = 1, ACT_SRELU = 2 };
+
+template <int ACT>
+__device__ __forceinline__ float act_value(float g, float alpha, int gtanh) {
+  if constexpr (ACT == ACT_SWIGLU) {
+    return g * sigm(alpha * g);
+  } else if constexpr (ACT == ACT_GEGLU) {
     if (gtanh) {
       const float c = 0.7978845608028654f;
       return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
     }
     return 0.5f * g * (1.0f + erff(g * 0.7071067811865476f));
+  } else {
+    float r = fmaxf(g, 0.0f);
+    return r * r;
   }
-  float r = fmaxf(g, 0.0f);  // squared ReLU
-  return r * r;
 }
 
-__device__ __forceinline__ float act_bwd(float g, int act, float alpha, int gtanh) {
-  if (act == MOE_ACT_SWIGLU) {
-    float s = sigm(alpha * g);
-    return s + alpha * g * s * (1.0f - s);
-  }
-  if (act == MOE_ACT_GEGLU) {
+template <int ACT>
+__device__ __forceinline__ void act_value_grad(float g, float alpha, int gtanh, float& a,
+                                               float& da) {
+  if constexpr (ACT == ACT_SWIGLU) {
+    const float sg = sigm(alpha * g);
+    a = g * sg;
+    da = sg + alpha * g * sg * (1.0f - sg);
+  } else if constexpr (ACT == ACT_GEGLU) {
     if (gtanh) {
       const float c = 0.7978845608028654f;
-      float th = tanhf(c * (g + 0.044715f * g * g * g));
-      return 0.5f * (1.0f + th) + 0.5f * g * (1.0f - th * th) * c * (1.0f + 0.134145f * g * g);
+      const float th = tanhf(c * (g + 0.044715f * g * g * g));
+      a = 0.5f * g * (1.0f + th);
+      da = 0.5f * (1.0f + th) + 0.5f * g * (1.0f - th * th) * c * (1.0f + 0.134145f * g * g);
+    } else {
+      const float cdf = 0.5f * (1.0f + erff(g * 0.7071067811865476f));
+      a = g * cdf;
+      da = cdf + g * expf(-0.5f * g * g) * 0.3989422804014327f;
     }
-    return 0.5f * (1.0f + erff(g * 0.7071067811865476f)) +
-           g * expf(-0.5f * g * g) * 0.3989422804014327f;
+  } else {
+    const float r = fmaxf(g, 0.0f);
+    a = r * r;
+    da = 2.0f * r;
   }
-  return 2.0f * fmaxf(g, 0.0f);
+}
+
+constexpr int epi_act(int e) {
+  return (e == EPI_GEGLU_FWD || e == EPI_GEGLU_BWD) ? ACT_GEGLU
+         : (e == EPI_SRELU_FWD || e == EPI_SRELU_BWD) ? ACT_SRELU : ACT_SWIGLU;
 }
 
 // ------------------------------------------------------------------ tile loaders
 
-// K-contiguous operand: ROWS x 128 bytes of K from X[row][k] (row stride ld).
-template <class EL, int ROWS, int THREADS>
-struct LoaderK {
-  typedef typename EL::storage S;
-  static constexpr int NCH = ROWS * 8;
-  static constexpr int PER = (NCH + THREADS - 1) / THREADS;
-  u32x4 r[PER];
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-  __device__ __forceinline__ void load(const S* X, long long ld, int r0, int rlim, int k0,
-                                       int klim, int tid) {
+// Byte offset that a buffer access treats as out of range (it returns zeros).
+static constexpr uint32_t OOB = 0x80000000u;
+
+// Operand tiles go global -> LDS directly (buffer_load ... lds, 16 bytes per
+// lane): no staging registers, and elements outside the operand (rows past a
+// segment end, columns past N, k past K) read as zeros through the buffer
+// range check instead of branches.  A wave instruction fills 1 KB of LDS;
+// each lane chooses which 16-byte global chunk lands in its 16 LDS bytes,
+// which is how the swizzled LDS layouts below are produced.
+//
+// Interface of both loaders: setup(X, ld, mn0, mnlim, kend, tid) once per
+// tile, issue(stage, k0) once per k-step of 128 bytes of K.
+
+// K-contiguous operand X[mn][k]: LDS row = one mn index, 128 bytes of K as
+// eight 16-byte chunks, chunk c of row r at slot c ^ (r & 7), so a quarter
+// wave reading eight rows at one chunk touches all 32 banks.
+template <class EL, int ROWS, int THREADS>
+struct DmaK {
+  typedef typename EL::storage S;
+  static constexpr int NW = THREADS / 64;
+  static constexpr int PER = ROWS / 8 / NW;
+  static_assert(ROWS % (8 * NW) == 0, "rows must split evenly over the waves");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[PER];
+  int kc, K;
+
+  __device__ __forceinline__ void setup(const S* X, long long ld, int r0, int rlim, int Kdim,
+                                        int tid) {
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X) + (size_t)r0 * ld, (short)0,
+                                           0x7ffffff0, 0x00020000);
+    const int rsub = lane >> 3, c = (lane & 7) ^ rsub;
+    kc = c * EL::VEC;
+    K = Kdim;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int q = tid + i * THREADS;
-      int row = q >> 3, c = q & 7;
-      int gr = r0 + row, gk = k0 + c * EL::VEC;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((NCH % THREADS == 0 || q < NCH) && gr < rlim && gk < klim)
-        v = *reinterpret_cast<const u32x4*>(X + (size_t)gr * ld + gk);
-      r[i] = v;
+      int row = 8 * (w * PER + i) + rsub;
+      voff[i] = (r0 + row < rlim) ? (uint32_t)(((size_t)row * ld + kc) * sizeof(S)) : OOB;
     }
   }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+  __device__ __forceinline__ void issue(u32x4* stage, int k0) const {
+    // the LDS destination (M0) must be wave-uniform: derive the wave id so the
+    // compiler can see that
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t kbad = (k0 + kc < K) ? 0u : OOB;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int q = tid + i * THREADS;
-      if (NCH % THREADS == 0 || q < NCH) {
-        int row = q >> 3, c = q & 7;
-        lds[row * 8 + (c ^ (row & 7))] = r[i];
-      }
-    }
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(stage + (w * PER + i) * 64), 16,
+                                               (int)(voff[i] | kbad), k0 * (int)sizeof(S), 0, 0);
   }
 };
 
-// MN-contiguous operand: X[k][mn] (row stride ld); the tile covers ROWS values
-// of mn and 128 bytes of k.  A job is a VEC(k) x VEC(mn) block: VEC 16-byte
-// loads along mn, transposed in registers into VEC 16-byte chunks along k.
+// MN-contiguous operand X[k][mn]: LDS row = one k index holding the tile's
+// ROWS values of mn.  For bf16, 16-byte chunk c of k-row k sits at slot
+// c ^ ((k & 3) << 2): the transposed fragment reads below touch 4 consecutive
+// k-rows x 64 bytes per half wave, which this spreads over distinct banks.
 template <class EL, int ROWS, int THREADS>
-struct LoaderMN {
+struct DmaMN {
   typedef typename EL::storage S;
   static constexpr int V = EL::VEC;
-  static constexpr int JOBS = (ROWS / V) * 8;
-  static constexpr int PER = (JOBS + THREADS - 1) / THREADS;
-  u32x4 r[PER][V];
+  static constexpr int ROWB = ROWS * (int)sizeof(S);   // bytes per k-row
+  static constexpr int BK = 128 / (int)sizeof(S);       // k-rows per step
+  static constexpr int INSTR = BK * ROWB / 1024;
+  static constexpr int NW = THREADS / 64;
+  static constexpr int PER = INSTR / NW;
+  static constexpr int RPI = 1024 / ROWB;                // k-rows per wave instruction
+  static constexpr bool SWZ = sizeof(S) == 2;
+  static_assert(ROWB <= 1024 && INSTR % NW == 0, "tile does not split into wave loads");
+  static_assert(!SWZ || ROWB % 256 == 0, "the bf16 swizzle needs 16 chunks per k-row");
+  const S* X;
+  long long ld;
+  int c0, clim, kend, krl, slot;
 
-  __device__ __forceinline__ void load(const S* X, long long ld, int c0, int clim, int k0,
-                                       int klim, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int job = tid + i * THREADS;
-      int kb = job & 7, mb = job >> 3;
-      int gmn = c0 + mb * V;
-      bool ok = (JOBS % THREADS == 0 || job < JOBS) && gmn < clim;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        int gk = k0 + kb * V + j;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok && gk < klim) v = *reinterpret_cast<const u32x4*>(X + (size_t)gk * ld + gmn);
-        r[i][j] = v;
-      }
-    }
+  __device__ __forceinline__ void setup(const S* X_, long long ld_, int c0_, int clim_, int kend_,
+                                        int tid) {
+    X = X_;
+    ld = ld_;
+    c0 = c0_;
+    clim = clim_;
+    kend = kend_;
+    const int lane = tid & 63;
+    krl = (16 * lane) / ROWB;
+    slot = ((16 * lane) % ROWB) / 16;
   }
-  __device__ __forceinline__ void store(u32x4* lds, int tid) const {
+  __device__ __forceinline__ void issue(u32x4* stage, int k0) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<S*>(X) + (size_t)k0 * ld + c0, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int job = tid + i * THREADS;
-      if (JOBS % THREADS == 0 || job < JOBS) {
-        int kb = job & 7, mb = job >> 3;
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          u32x4 o;
-          if constexpr (V == 8) {
-            // element e of each of the 8 k-rows: bf16 halves of dword e/2
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              uint32_t lo = r[i][2 * h][e >> 1], hi = r[i][2 * h + 1][e >> 1];
-              o[h] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 4; ++h) o[h] = r[i][h][e];
-          }
-          int row = mb * V + e;
-          lds[row * 8 + (kb ^ (row & 7))] = o;
-        }
-      }
+      const int kr = (w * PER + i) * RPI + krl;
+      const int chunk = SWZ ? (slot ^ ((kr & 3) << 2)) : slot;
+      const bool ok = (k0 + kr < kend) && (c0 + chunk * V < clim);
+      const uint32_t vo = ok ? (uint32_t)(((size_t)kr * ld + chunk * V) * sizeof(S)) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(stage + (w * PER + i) * 64), 16,
+                                               (int)vo, 0, 0, 0);
     }
   }
 };
 
-template <bool KMAJOR, class EL, int ROWS, int THREADS>
-struct Loader;
-template <class EL, int ROWS, int THREADS>
-struct Loader<true, EL, ROWS, THREADS> : LoaderK<EL, ROWS, THREADS> {};
-template <class EL, int ROWS, int THREADS>
-struct Loader<false, EL, ROWS, THREADS> : LoaderMN<EL, ROWS, THREADS> {};
+// MFMA fragment of 32 mn-rows starting at r0, k sub-step s (16 k for bf16,
+// 8 k for fp32): lane l holds mn = r0 + (l & 31) and the 16-byte k-chunk
+// 2 s + (l >> 5).
+template <bool KMAJ, class EL, int ROWS>
+struct Frag;
+
+template <class EL, int ROWS>
+struct Frag<true, EL, ROWS> {
+  __device__ __forceinline__ static u32x4 load(const u32x4* st, int r0, int s, int lane) {
+    const int row = r0 + (lane & 31), ch = 2 * s + (lane >> 5);
+    return st[row * 8 + (ch ^ (row & 7))];
+  }
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// bf16 from a [k][mn] tile with ds_read_b64_tr_b16.  Within each group of 16
+// lanes, lane i receives element (i mod 4) of the 8-byte segments addressed by
+// lanes 4 q + i / 4, q = 0..3.  Lane j = 16 g + 4 q + r therefore addresses
+// k-row kb + q, mn columns mb + 4 r .. + 3, so that every lane i of the group
+// ends up with k = kb .. kb + 3 of mn = mb + i: half of its MFMA fragment.
+template <int ROWS>
+struct Frag<false, BF16, ROWS> {
+  __device__ __forceinline__ static u32x4 load(const u32x4* st, int r0, int s, int lane) {
+    constexpr int ROWB = ROWS * 2;
+    const int g = lane >> 4, q = (lane >> 2) & 3, r = lane & 3;
+    const int mn = r0 + 16 * (g & 1) + 4 * r;
+    const char* base = reinterpret_cast<const char*>(st);
+    u32x4 out;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = 16 * s + 8 * (g >> 1) + 4 * half + q;
+      const int chunk = (mn >> 3) ^ (q << 2);  // k & 3 == q
+      const char* p = base + k * ROWB + chunk * 16 + (mn & 7) * 2;
+      i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(p));
+      u32x2 w = __builtin_bit_cast(u32x2, v);
+      out[2 * half] = w[0];
+      out[2 * half + 1] = w[1];
+    }
+    return out;
+  }
+};
+
+// fp32 from a [k][mn] tile: the fp32 MFMA takes one value per lane, element q
+// of the lane's k-chunk, i.e. k = 4 (2 s + (l >> 5)) + q.
+template <int ROWS>
+struct Frag<false, F32, ROWS> {
+  __device__ __forceinline__ static u32x4 load(const u32x4* st, int r0, int s, int lane) {
+    const float* base = reinterpret_cast<const float*>(st);
+    const int col = r0 + (lane & 31), kb = 4 * (2 * s + (lane >> 5));
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(base[(kb + q) * ROWS + col]);
+    return out;
+  }
+};
 
 // ------------------------------------------------------------------ MFMA step
 
@@ -208,6 +311,176 @@ __device__ __forceinline__ void mma(f32x16& acc, const u32x4& b, const u32x4& a,
                                                0, 0, 0);
 }
 
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.  Used where
+// accumulators are indexed, so that no index is ever a run-time value (a
+// run-time index would move the accumulator array to private memory).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// ------------------------------------------------------------------ epilogues
+//
+// Each helper handles one 32 x 32 accumulator block of one lane: the lane's
+// row, and columns c0 + 8 g + q (g, q = 0..3), acc[4 g + q].  Pointers are
+// the lane's row of each tensor; they are distinct tensors (noalias), so the
+// compiler may issue every load of a block before its stores.
+
+template <class S>
+__device__ __forceinline__ void epi_store(S* __restrict__ C, const float* __restrict__ bias,
+                                          const f32x16& acc, int c0, int N) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = acc[4 * g + q] + (bias ? bias[col + q] : 0.0f);
+    store4(C + col, v);
+  }
+}
+
+__device__ __forceinline__ void epi_store_f32(float* __restrict__ C, const f32x16& acc, int c0,
+                                              int N, int accumulate) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    float v[4];
+    if (accumulate) load4(C + col, v);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = (accumulate ? v[q] : 0.0f) + acc[4 * g + q];
+    store4(C + col, v);
+  }
+}
+
+// FC1 + GLU: gate block (packed columns c0 + ...) and the linear block 32
+// columns further; A column of packed gate column c is 32 (c / 64) + c % 64.
+template <int ACT, class S>
+__device__ __forceinline__ void epi_glu_fwd(S* __restrict__ Hrow, S* __restrict__ Arow,
+                                            const float* __restrict__ bias,
+                                            const f32x16& accg, const f32x16& accl, int c0,
+                                            int N, float L, float alpha, int gtanh) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    float gv[4], lv[4], o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      gv[q] = accg[4 * g + q] + (bias ? bias[col + q] : 0.0f);
+      lv[q] = accl[4 * g + q] + (bias ? bias[col + 32 + q] : 0.0f);
+    }
+    if (Hrow) {
+      store4(Hrow + col, gv);
+      store4(Hrow + col + 32, lv);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float gt = gv[q], li = lv[q];
+      if (L > 0.0f) {
+        gt = fminf(gt, L);
+        li = fminf(fmaxf(li, -L), L);
+      }
+      o[q] = act_value<ACT>(gt, alpha, gtanh) * li;
+    }
+    store4(Arow + (col >> 6) * 32 + (col & 31), o);
+  }
+}
+
+// FC2 dgrad + dGLU: acc = dA at A columns c0 + ...; gate of A column c sits at
+// packed column 64 (c / 32) + c % 32 and the linear value 32 columns further.
+template <int ACT, class S>
+__device__ __forceinline__ void epi_glu_bwd(const S* __restrict__ Hrow, S* __restrict__ Drow,
+                                            const f32x16& acc, int c0, int N, float L,
+                                            float alpha, int gtanh) {
+  float hg[4][4], hl[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    const int pg = (col >> 5) * 64 + (col & 31);
+    if (col < N) {
+      load4(Hrow + pg, hg[g]);
+      load4(Hrow + pg + 32, hl[g]);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    const int pg = (col >> 5) * 64 + (col & 31);
+    float dg[4], dl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float gt = hg[g][q], li = hl[g][q], mg = 1.0f, ml = 1.0f;
+      if (L > 0.0f) {
+        mg = gt <= L ? 1.0f : 0.0f;
+        ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
+        gt = fminf(gt, L);
+        li = fminf(fmaxf(li, -L), L);
+      }
+      float a, da_dg;
+      act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
+      const float d = acc[4 * g + q];
+      dg[q] = d * li * da_dg * mg;
+      dl[q] = d * a * ml;
+    }
+    store4(Drow + pg, dg);
+    store4(Drow + pg + 32, dl);
+  }
+}
+
+// FC1 + squared ReLU (not gated): H = acc + b1, A = relu(min(H, L))^2.
+template <class S>
+__device__ __forceinline__ void epi_srelu_fwd(S* __restrict__ Hrow, S* __restrict__ Arow,
+                                              const float* __restrict__ bias, const f32x16& acc,
+                                              int c0, int N, float L) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    float v[4], o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = acc[4 * g + q] + (bias ? bias[col + q] : 0.0f);
+      const float h = L > 0.0f ? fminf(v[q], L) : v[q];
+      const float r = fmaxf(h, 0.0f);
+      o[q] = r * r;
+    }
+    if (Hrow) store4(Hrow + col, v);
+    store4(Arow + col, o);
+  }
+}
+
+// FC2 dgrad + squared-ReLU backward: dH = dA * 2 relu(h) * [h <= L].
+template <class S>
+__device__ __forceinline__ void epi_srelu_bwd(const S* __restrict__ Hrow, S* __restrict__ Drow,
+                                              const f32x16& acc, int c0, int N, float L) {
+  float hv[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    if (c0 + 8 * g < N) load4(Hrow + c0 + 8 * g, hv[g]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float h = hv[g][q], m = 1.0f;
+      if (L > 0.0f) {
+        m = h <= L ? 1.0f : 0.0f;
+        h = fminf(h, L);
+      }
+      o[q] = acc[4 * g + q] * 2.0f * fmaxf(h, 0.0f) * m;
+    }
+    store4(Drow + col, o);
+  }
+}
+
 // ------------------------------------------------------------------ the kernel
 
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI, int BM, int BN, int WGM, int WGN>
@@ -219,7 +492,7 @@ struct GemmCfg {
   static constexpr int GM = 8;  // M-tiles per band of the tile order
   static constexpr size_t LDS_BYTES = 2 * (size_t)(BM + BN) * 128;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(EPI != EPI_GLU_FWD || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
+  static_assert(!epi_glu_fwd(EPI) || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
 };
 
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI, int BM, int BN, int WGM, int WGN>
@@ -232,7 +505,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_tab[MOE_MAX_EXPERTS + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int E = p.E;
 
@@ -330,6 +604,15 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
       kend = max(s_off[e + 1], kbeg);
     }
 
+    // The tile coordinates come out of LDS tables but are the same on every
+    // lane: say so, so that addresses and buffer descriptors live in SGPRs.
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    mlim = __builtin_amdgcn_readfirstlane(mlim);
+    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+    kend = __builtin_amdgcn_readfirstlane(kend);
+
     // ---- main loop ----
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -342,185 +625,100 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
     const S* A = reinterpret_cast<const S*>(p.a);
     const S* B = reinterpret_cast<const S*>(p.b);
     if constexpr (GROUP == RAGGED_M) B += (size_t)e * p.b_expert_stride;
-    Loader<AKM, EL, BM, THREADS> la;
-    Loader<BKM, EL, BN, THREADS> lb;
     const int nk = (kend - kbeg + BK - 1) / BK;
 
-    auto load_tiles = [&](int k0) {
-      if constexpr (GROUP == RAGGED_M) {
-        la.load(A, p.lda, m0, mlim, k0, kend, tid);     // A [R][K]
-      } else {
-        la.load(A, p.lda, m0, mlim, k0, kend, tid);     // A [rows=K][M]
-      }
-      lb.load(B, p.ldb, n0, p.N, k0, kend, tid);
-    };
+    // Both operands go global -> LDS by DMA; a step issues the loads of step
+    // kt + 1, runs the MFMAs of step kt, and ends with one barrier (which also
+    // waits for this wave's loads).
+    typedef typename std::conditional<AKM, DmaK<EL, BM, THREADS>, DmaMN<EL, BM, THREADS>>::type
+        LoadA;
+    typedef typename std::conditional<BKM, DmaK<EL, BN, THREADS>, DmaMN<EL, BN, THREADS>>::type
+        LoadB;
+    LoadA la;
+    LoadB lb;
+    la.setup(A, p.lda, m0, mlim, kend, tid);
+    lb.setup(B, p.ldb, n0, p.N, kend, tid);
 
     if (nk > 0) {
-      load_tiles(kbeg);
       __syncthreads();  // the previous tile's readers are done with buf0
-      la.store(buf0, tid);
-      lb.store(buf0 + BM * 8, tid);
+      la.issue(buf0, kbeg);
+      lb.issue(buf0 + BM * 8, kbeg);
       __syncthreads();
       for (int kt = 0; kt < nk; ++kt) {
         u32x4* cur = (kt & 1) ? buf1 : buf0;
         u32x4* nxt = (kt & 1) ? buf0 : buf1;
-        if (kt + 1 < nk) load_tiles(kbeg + (kt + 1) * BK);
+        if (kt + 1 < nk) {
+          la.issue(nxt, kbeg + (kt + 1) * BK);
+          lb.issue(nxt + BM * 8, kbeg + (kt + 1) * BK);
+        }
         const u32x4* As = cur;
         const u32x4* Bs = cur + BM * 8;
+        // fragments of sub-step s + 1 are read while the MFMAs of s run
+        u32x4 af[2][TM], bfr[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[0][i] = Frag<AKM, EL, BM>::load(As, wm * C::WTM + 32 * i, 0, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[0][j] = Frag<BKM, EL, BN>::load(Bs, wn * C::WTN + 32 * j, 0, lane);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int ch = 2 * s + (lane >> 5);
-          u32x4 af[TM], bfr[TN];
+          if (s < 3) {
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            int row = wm * C::WTM + 32 * i + (lane & 31);
-            af[i] = As[row * 8 + (ch ^ (row & 7))];
-          }
+            for (int i = 0; i < TM; ++i)
+              af[(s + 1) & 1][i] = Frag<AKM, EL, BM>::load(As, wm * C::WTM + 32 * i, s + 1, lane);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            int row = wn * C::WTN + 32 * j + (lane & 31);
-            bfr[j] = Bs[row * 8 + (ch ^ (row & 7))];
+            for (int j = 0; j < TN; ++j)
+              bfr[(s + 1) & 1][j] = Frag<BKM, EL, BN>::load(Bs, wn * C::WTN + 32 * j, s + 1, lane);
           }
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) mma(acc[i][j], bfr[j], af[i], EL());
-        }
-        if (kt + 1 < nk) {
-          la.store(nxt, tid);
-          lb.store(nxt + BM * 8, tid);
+            for (int j = 0; j < TN; ++j) mma(acc[i][j], bfr[s & 1][j], af[s & 1][i], EL());
         }
         __syncthreads();
       }
     }
 
     // ---- epilogue: lane holds rows (lane & 31) + 32 i, columns 32 j + 8 g + 4 h + q ----
-    const int h4 = 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    const int cw = n0 + wn * C::WTN + 4 * (lane >> 5);  // column of the lane's first value
+    static_for<0, TM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       const int row = m0 + wm * C::WTM + 32 * i + (lane & 31);
-      if (row >= mlim) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * C::WTN + 32 * j + 8 * g + h4;
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+      if (row < mlim) {
+        static_for<0, TN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const int c0 = cw + 32 * j;
           if constexpr (EPI == EPI_STORE && GROUP == RAGGED_M) {
-            if (col < p.N) {
-              if (p.bias) {
-                const float* bb = p.bias + (size_t)e * p.ld_bias + col;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] += bb[q];
-              }
-              store4(reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc + col, v);
-            }
-          } else if constexpr (EPI == EPI_STORE && GROUP == RAGGED_K) {
-            if (col < p.N) {
-              float* cp = reinterpret_cast<float*>(p.c) + (size_t)e * p.c_expert_stride +
-                          (size_t)row * p.ldc + col;
-              if (p.accumulate) {
-                float o[4];
-                load4(cp, o);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] += o[q];
-              }
-              store4(cp, v);
-            }
-          } else if constexpr (EPI == EPI_GLU_FWD) {
-            // j even: gate chunk; j + 1: the matching linear chunk (32 columns later)
-            if ((j & 1) == 0 && col < p.N) {
-              float lv[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) lv[q] = acc[i][j + 1][4 * g + q];
-              const int colL = col + 32;
-              if (p.bias) {
-                const float* bb = p.bias + (size_t)e * p.ld_bias;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  v[q] += bb[col + q];
-                  lv[q] += bb[colL + q];
-                }
-              }
-              if (p.aux) {
-                S* H = reinterpret_cast<S*>(p.aux) + (size_t)row * p.ld_aux;
-                store4(H + col, v);
-                store4(H + colL, lv);
-              }
-              float o[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float gt = v[q], li = lv[q];
-                if (p.clamp > 0.0f) {
-                  gt = fminf(gt, p.clamp);
-                  li = fminf(fmaxf(li, -p.clamp), p.clamp);
-                }
-                o[q] = act_fwd(gt, p.act, p.alpha, p.gelu_tanh) * li;
-              }
-              const int acol = (col >> 6) * 32 + (col & 31);
-              store4(reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc + acol, o);
-            }
-          } else if constexpr (EPI == EPI_GLU_BWD) {
-            if (col < p.N) {
-              const int pg = (col >> 5) * 64 + (col & 31), pl = pg + 32;
-              const S* H = reinterpret_cast<const S*>(p.aux) + (size_t)row * p.ld_aux;
-              float hg[4], hl[4], dg[4], dl[4];
-              load4(H + pg, hg);
-              load4(H + pl, hl);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float gt = hg[q], li = hl[q], mg = 1.0f, ml = 1.0f;
-                if (p.clamp > 0.0f) {
-                  mg = gt <= p.clamp ? 1.0f : 0.0f;
-                  ml = (li >= -p.clamp && li <= p.clamp) ? 1.0f : 0.0f;
-                  gt = fminf(gt, p.clamp);
-                  li = fminf(fmaxf(li, -p.clamp), p.clamp);
-                }
-                dg[q] = v[q] * li * act_bwd(gt, p.act, p.alpha, p.gelu_tanh) * mg;
-                dl[q] = v[q] * act_fwd(gt, p.act, p.alpha, p.gelu_tanh) * ml;
-              }
-              S* D = reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc;
-              store4(D + pg, dg);
-              store4(D + pl, dl);
-            }
+            epi_store<S>(reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc,
+                         p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], c0, p.N);
+          } else if constexpr (EPI == EPI_STORE) {
+            epi_store_f32(reinterpret_cast<float*>(p.c) + (size_t)e * p.c_expert_stride +
+                              (size_t)row * p.ldc,
+                          acc[i][j], c0, p.N, p.accumulate);
+          } else if constexpr (epi_glu_fwd(EPI)) {
+            if constexpr ((j & 1) == 0)
+              epi_glu_fwd<epi_act(EPI), S>(
+                  p.aux ? reinterpret_cast<S*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
+                  reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc,
+                  p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], acc[i][j + 1],
+                  c0, p.N, p.clamp, p.alpha, p.gelu_tanh);
+          } else if constexpr (epi_glu_bwd(EPI)) {
+            epi_glu_bwd<epi_act(EPI), S>(
+                reinterpret_cast<const S*>(p.aux) + (size_t)row * p.ld_aux,
+                reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0, p.N, p.clamp,
+                p.alpha, p.gelu_tanh);
           } else if constexpr (EPI == EPI_SRELU_FWD) {
-            if (col < p.N) {
-              if (p.bias) {
-                const float* bb = p.bias + (size_t)e * p.ld_bias + col;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] += bb[q];
-              }
-              if (p.aux) store4(reinterpret_cast<S*>(p.aux) + (size_t)row * p.ld_aux + col, v);
-              float o[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float hv = p.clamp > 0.0f ? fminf(v[q], p.clamp) : v[q];
-                float r = fmaxf(hv, 0.0f);
-                o[q] = r * r;
-              }
-              store4(reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc + col, o);
-            }
+            epi_srelu_fwd<S>(
+                p.aux ? reinterpret_cast<S*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
+                reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc,
+                p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], c0, p.N, p.clamp);
           } else if constexpr (EPI == EPI_SRELU_BWD) {
-            if (col < p.N) {
-              float hv[4], o[4];
-              load4(reinterpret_cast<const S*>(p.aux) + (size_t)row * p.ld_aux + col, hv);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float hq = hv[q], m = 1.0f;
-                if (p.clamp > 0.0f) {
-                  m = hq <= p.clamp ? 1.0f : 0.0f;
-                  hq = fminf(hq, p.clamp);
-                }
-                o[q] = v[q] * 2.0f * fmaxf(hq, 0.0f) * m;
-              }
-              store4(reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc + col, o);
-            }
+            epi_srelu_bwd<S>(reinterpret_cast<const S*>(p.aux) + (size_t)row * p.ld_aux,
+                             reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0,
+                             p.N, p.clamp);
           }
-        }
+        });
       }
-    }
+    });
   }
 }
 
@@ -565,8 +763,19 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
   }
 }
 
+// MOE_GEMM_TILE=128 or 256 in the environment overrides the tile-shape choice
+// (for tuning and for testing both shapes on small problems).
+inline bool tile_override(bool big) {
+  const char* v = getenv("MOE_GEMM_TILE");
+  if (!v) return big;
+  if (v[0] == '1') return false;
+  if (v[0] == '2') return true;
+  return big;
+}
+
 template <bool AKM, bool BKM, int GROUP, int EPI>
 moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
+  big = tile_override(big);
   if (dtype == MOE_BF16) return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
   return dispatch_tiles<F32, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
 }
@@ -625,7 +834,10 @@ moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream)
   p.gelu_tanh = a->gelu_tanh;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool big = big_ragged_m(a->R, a->E, n1);
-  if (gated) return dispatch<true, true, RAGGED_M, EPI_GLU_FWD>(a->dtype, p, big, a->max_cus, s);
+  if (a->act == MOE_ACT_SWIGLU)
+    return dispatch<true, true, RAGGED_M, EPI_SWIGLU_FWD>(a->dtype, p, big, a->max_cus, s);
+  if (a->act == MOE_ACT_GEGLU)
+    return dispatch<true, true, RAGGED_M, EPI_GEGLU_FWD>(a->dtype, p, big, a->max_cus, s);
   return dispatch<true, true, RAGGED_M, EPI_SRELU_FWD>(a->dtype, p, big, a->max_cus, s);
 }
 
@@ -687,7 +899,10 @@ moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream)
   p.gelu_tanh = a->gelu_tanh;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool big = big_ragged_m(a->R, a->E, a->f);
-  if (gated) return dispatch<true, false, RAGGED_M, EPI_GLU_BWD>(a->dtype, p, big, a->max_cus, s);
+  if (a->act == MOE_ACT_SWIGLU)
+    return dispatch<true, false, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+  if (a->act == MOE_ACT_GEGLU)
+    return dispatch<true, false, RAGGED_M, EPI_GEGLU_BWD>(a->dtype, p, big, a->max_cus, s);
   return dispatch<true, false, RAGGED_M, EPI_SRELU_BWD>(a->dtype, p, big, a->max_cus, s);
 }
 

@@ -91,3 +91,24 @@ def offsets_of(counts):
     off = np.zeros(len(counts) + 1, dtype=np.int32)
     off[1:] = np.cumsum(counts)
     return off
+
+
+def rel_l2(g, o):
+    """||g - o||_2 / ||o||_2: the relative error of a float32 result."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    n = float(np.linalg.norm(o))
+    d = float(np.linalg.norm(g - o))
+    return d / n if n > 0 else (0.0 if d == 0 else math.inf)
+
+
+def ulp_err(g, o):
+    """max |g - o| / (one bf16 ulp at o + 1e-3 rms(o)): elementwise distance in bf16 ulps."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    if o.size == 0:
+        return 0.0
+    den = 2.0 * half_ulp_bf16(o) + 1e-3 * rms(o)
+    return float(np.max(np.abs(g - o) / den))

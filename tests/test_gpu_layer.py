@@ -3,17 +3,27 @@ oracle chain, on seeded synthetic inputs of the workloads' structure at sizes
 the oracle finishes in seconds; plus graph capture / replay and determinism.
 
 The oracle chain rounds every tensor the library stores (H, A, Y, dY, dH,
-dXp) to the same storage type, so what remains is accumulation order and the
-final rounding.  Tolerances: routing and layout bit-exact; gates 1e-5;
-float32 workloads 1e-5 everywhere; bf16 workloads 2e-2 of max|err|/rms for
-every layer output (the bf16 rounding floor of each is printed beside it)."""
+dXp) to the same storage type, so what remains is accumulation order, the
+final rounding, and the occasional one-ulp flip where the library's float32
+value and the oracle's float64 value round to neighbouring bf16 values.
+Tolerances:
+  * routing and layout: bit-exact; gates: relative L2 <= 1e-5;
+  * float32 workloads: every tensor relative L2 <= 1e-5;
+  * bf16 workloads, layer outputs stored in bf16 (out, dX): max |err| beyond
+    the output's own half-ulp rounding, / rms, <= 2e-2 (raw max|err|/rms and
+    the rounding floor are printed beside it);
+  * bf16 workloads, float32 gradients (dW1, dW2, db1, db2, dgate, dlogits):
+    max |err| / rms <= 2e-2;
+  * bf16 workloads, stored intermediates (H, A, Y, dY, dH, dXp): every
+    element within 8 bf16 ulps (+1e-3 rms) of the oracle chain; each of these
+    is checked tightly on identical inputs in the per-entry-point tests."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 from oracle import moe as om
-from gpu_util import bf16_excess, bf16_floor, host, norm_err, note
+from gpu_util import bf16_excess, bf16_floor, host, norm_err, note, rel_l2, ulp_err
 
 pytestmark = pytest.mark.gpu
 G = 32
@@ -101,7 +111,6 @@ def test_layer_parity(name):
     torch.cuda.synchronize()
     fwd, bwd = _oracle(cfg, inp)
     f32 = cfg.dtype == "f32"
-    tol = 1e-5 if f32 else 2e-2
 
     # routing and layout: bit-exact
     np.testing.assert_array_equal(host(L.topk_idx), fwd["topk_idx"])
@@ -110,23 +119,36 @@ def test_layer_parity(name):
     np.testing.assert_array_equal(host(L.row_map), fwd["row_map"])
     np.testing.assert_array_equal(host(L.src_row), fwd["src_row"])
     np.testing.assert_array_equal(host(L.xp), fwd["xp"])
-    assert norm_err(host(L.topk_w), fwd["topk_w"]) <= 1e-5
+    assert rel_l2(host(L.topk_w), fwd["topk_w"]) <= 1e-5
     assert int(L.err.item()) == 0
 
     report = {}
 
-    def check(label, got, ref, exact_ref=None, tol_=tol):
-        e = norm_err(got, ref)
+    def check(label, got, ref):
+        """A layer output (bf16 storage: out, dX) or a float32 gradient."""
+        if f32:
+            e = rel_l2(got, ref)
+            report[label] = e
+            report[label + "_max"] = norm_err(got, ref)
+            assert e <= 1e-5, (label, e, report)
+            return
+        raw = norm_err(got, ref)
+        bf16_store = label in ("out", "dX")
+        e = bf16_excess(got, ref) if bf16_store else raw
         report[label] = e
-        if not f32:
+        if bf16_store:
+            report[label + "_raw"] = raw
             report[label + "_floor"] = bf16_floor(ref)
-        assert e <= tol_, (label, e, report)
+        assert e <= 2e-2, (label, e, report)
 
     def check_stored(label, got, ref_exact):
-        # intermediates stored in bf16 / f32: error beyond their own rounding
-        e = norm_err(got, ref_exact) if f32 else bf16_excess(got, ref_exact)
+        if f32:
+            e = rel_l2(got, ref_exact)
+            assert e <= 1e-5, (label, e)
+        else:
+            e = ulp_err(got, ref_exact)
+            assert e <= 8.0, (label, e)
         report[label] = e
-        assert e <= (tol if f32 else tol / 4), (label, e)
 
     check_stored("H", host(L.H), _pack_cols(fwd["H_exact"], cfg))
     check_stored("A", host(L.A), fwd["A_exact"])

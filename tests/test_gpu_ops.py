@@ -1,9 +1,10 @@
 """Per-entry-point parity of the HIP library against the CPU oracle.
 
 Each test feeds the same seeded inputs to a library call (through the C ABI)
-and to the oracle, then compares: integer and index outputs bit for bit,
-float32 outputs to 1e-5 of max |err| / rms, bf16 outputs by their error
-beyond their own bf16 rounding (<= 2e-2 of rms; in practice far less).
+and to the oracle, then compares: integer and index outputs bit for bit;
+float32 outputs by relative L2 error <= 1e-5 (max |err| / rms <= 1e-4 too);
+bf16 outputs by their max error beyond their own bf16 rounding, / rms
+(<= 5e-3 here, a quarter of the layer tolerance).
 Expert segment sizes include empty experts and tails around the tile sizes."""
 import numpy as np
 import pytest
@@ -11,7 +12,8 @@ import torch
 
 import synth
 from oracle import moe as om
-from gpu_util import (bf16_excess, dev, host, norm_err, note, offsets_of, rand_bf16, rand_f32)
+from gpu_util import (bf16_excess, dev, host, norm_err, note, offsets_of, rand_bf16, rand_f32,
+                      rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +32,15 @@ def _lib():
 
 TOL_BF16 = 2e-2
 TOL_F32 = 1e-5
+TOL_F32_MAX = 1e-4
+
+
 G = 32
+
+
+def f32_ok(got, ref):
+    return rel_l2(got, ref) <= TOL_F32 and norm_err(got, ref) <= TOL_F32_MAX
+
 
 # ragged segment sizes around the 128 / 256 tile heights, with empty experts
 COUNTS_SMALL = [0, 1, 31, 32, 33, 255, 256, 257, 0, 130]
@@ -53,7 +63,7 @@ def test_route_topk(score, normalize, E, k):
     idx, w = ops.moe_route_topk(dev(lg), k, score, normalize)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(idx), idx_o)
-    assert norm_err(host(w), w_o) <= TOL_F32
+    assert f32_ok(host(w), w_o)
     np.testing.assert_allclose(host(w), w_o, rtol=2e-6, atol=1e-7)
 
 
@@ -82,7 +92,7 @@ def test_route_topk_bwd(score, normalize):
     ref = om.route_topk_bwd(lg, idx_o, dw, score, normalize)
     got = ops.moe_route_topk_bwd(dev(lg), dev(idx_o.astype(np.int32)), dev(dw), score, normalize)
     torch.cuda.synchronize()
-    assert norm_err(host(got), ref) <= TOL_F32
+    assert f32_ok(host(got), ref)
 
 
 # ------------------------------------------------------------------ permute
@@ -196,8 +206,8 @@ def test_glu_fwd_f32(counts, d, f, act, clamp):
     else:
         Ao = om.glu_forward(Hc[:, :f], Hc[:, f:], act, clamp)
         Hp = om.repack_glu(Hc[None], G=G, axis=2)[0]
-    assert norm_err(host(H), Hp) <= TOL_F32
-    assert norm_err(host(A), Ao) <= TOL_F32
+    assert f32_ok(host(H), Hp)
+    assert f32_ok(host(A), Ao)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -219,7 +229,7 @@ def test_gemm_fwd(dtype, counts, N, K, bias):
     if dtype == "bf16":
         assert bf16_excess(host(y), ref) <= TOL_BF16 / 4
     else:
-        assert norm_err(host(y), ref) <= TOL_F32
+        assert f32_ok(host(y), ref)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -247,7 +257,7 @@ def test_glu_bwd(dtype, counts, d, f, act, clamp):
     if dtype == "bf16":
         assert bf16_excess(host(dh), ref) <= TOL_BF16 / 4
     else:
-        assert norm_err(host(dh), ref) <= TOL_F32
+        assert f32_ok(host(dh), ref)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -266,7 +276,7 @@ def test_gemm_dgrad(dtype, counts, N, K):
     if dtype == "bf16":
         assert bf16_excess(host(da), ref) <= TOL_BF16 / 4
     else:
-        assert norm_err(host(da), ref) <= TOL_F32
+        assert f32_ok(host(da), ref)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -286,12 +296,12 @@ def test_gemm_wgrad(dtype, counts, N, K):
     torch.cuda.synchronize()
     ref, refb = om.grouped_wgrad(gh, ah, off, with_bias=True)
     got = host(dw)
-    assert norm_err(got, ref) <= TOL_F32
-    assert norm_err(host(db), refb) <= TOL_F32
+    assert f32_ok(got, ref)
+    assert f32_ok(host(db), refb)
     for e, c in enumerate(counts):
         if c == 0:
             assert not got[e].any() and not host(db)[e].any()     # exact zeros
-    assert norm_err(host(dw2), 2 * ref) <= TOL_F32
+    assert f32_ok(host(dw2), 2 * ref)
 
 
 # ------------------------------------------------------------------ combine
@@ -321,10 +331,10 @@ def test_combine_and_backward(dtype, T, E, k, d):
         assert bf16_excess(host(unit), ref_unit) <= 1e-3
         assert bf16_excess(host(dy), rdy) <= 1e-3
     else:
-        assert norm_err(host(out), ref) <= TOL_F32
-        assert norm_err(host(unit), ref_unit) <= TOL_F32
-        assert norm_err(host(dy), rdy) <= TOL_F32
-    assert norm_err(host(dgate), rdg) <= TOL_F32
+        assert f32_ok(host(out), ref)
+        assert f32_ok(host(unit), ref_unit)
+        assert f32_ok(host(dy), rdy)
+    assert f32_ok(host(dgate), rdg)
 
 
 @pytest.mark.parametrize("k", [2, 4, 8])
