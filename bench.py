@@ -35,10 +35,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_fwdbwd")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens of the workload the CPU oracle runs (bounded sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
     return ap.parse_args()
 
 
@@ -67,6 +70,25 @@ def hbm_bytes(cfg):
                     "route_topk_bwd": T * E * 8 + T * k * 8,
                     "unpermute_dx": R * d * b + T * d * b + 4 * R})
     return out
+
+
+def recorded_traffic(cfg, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, scaled by the copy calibration; None when there is no
+    record for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"traffic_grouped_gemm_{cfg.name}.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+        with open(os.path.join(here, rec["kernel_source"]), "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if sha != rec.get("kernel_source_sha256") or kernel not in rec.get("kernels", {}):
+        return None
+    return rec["kernels"][kernel]["traffic_bytes"]
 
 
 def cpu_baseline(cfg, inp, tokens):
@@ -108,8 +130,16 @@ def main():
               f"--gpus {args.gpus} is not supported (see the sharding notes in DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
+    if args.calibration_copy:
+        n = args.calibration_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 3}), flush=True)
+        return
     import synth
     from ragged_grouped_gemm_amd import ops
     from ragged_grouped_gemm_amd.layer import MoEFFN, OpTimer
@@ -204,7 +234,7 @@ def main():
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None,
+                     "traffic": recorded_traffic(cfg, dom),
                      "flop_per_launch": flops[dom], "ms_per_launch": round(per_op[dom][1], 4)},
         "kernels": kernels,
     }
