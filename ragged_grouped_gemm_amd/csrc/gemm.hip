@@ -76,6 +76,7 @@ struct GemmArgs {
   float clamp, alpha;
   int act, gelu_tanh;
   int accumulate;
+  int gm;  // M-tiles per band of the tile order
 };
 
 // ------------------------------------------------------------------ activations
@@ -153,42 +154,61 @@ static constexpr uint32_t OOB = 0x80000000u;
 // Interface of both loaders: setup(X, ld, mn0, mnlim, kend, tid) once per
 // tile, issue(stage, k0) once per k-step of 128 bytes of K.
 
-// K-contiguous operand X[mn][k]: LDS row = one mn index, 128 bytes of K as
-// eight 16-byte chunks, chunk c of row r at slot c ^ (r & 7), so a quarter
-// wave reading eight rows at one chunk touches all 32 banks.
-template <class EL, int ROWS, int THREADS>
+// K-contiguous operand X[mn][k]: LDS row = one mn index holding BKB bytes of
+// K as CPR = BKB / 16 chunks of 16 bytes; chunk c of row r sits at slot
+// c ^ ((r >> RSH) & (CPR - 1)), RSH = log2(256 / BKB).  The 64 banks span 256
+// bytes, i.e. 256 / BKB rows.  A fragment read serves 16 lanes per LDS cycle,
+// one chunk of 16 consecutive rows: rows in the same 256-byte window sit at
+// different offsets in it, and rows of different windows get different XOR
+// keys, so the 16 lanes touch 16 distinct 16-byte bank groups.
+template <int BKB>
+struct KGeom {
+  static constexpr int CPR = BKB / 16;             // chunks per row
+  static constexpr int RPI = 1024 / BKB;           // rows per wave DMA instruction
+  static constexpr int RSH = BKB == 128 ? 1 : 2;   // log2(rows per 256-byte window)
+  static_assert(BKB == 64 || BKB == 128, "64- or 128-byte k steps");
+  __device__ __forceinline__ static int slot(int row, int chunk) {
+    return chunk ^ ((row >> RSH) & (CPR - 1));
+  }
+};
+
+template <class EL, int ROWS, int THREADS, int BKB>
 struct DmaK {
   typedef typename EL::storage S;
+  typedef KGeom<BKB> Gm;
   static constexpr int NW = THREADS / 64;
-  static constexpr int PER = ROWS / 8 / NW;
-  static_assert(ROWS % (8 * NW) == 0, "rows must split evenly over the waves");
+  static constexpr int PER = ROWS / Gm::RPI / NW;   // wave instructions per step
+  static_assert(ROWS % (Gm::RPI * NW) == 0, "rows must split evenly over the waves");
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[PER];
-  int kc, K;
+  int kc[PER];
+  int K;
 
   __device__ __forceinline__ void setup(const S* X, long long ld, int r0, int rlim, int Kdim,
                                         int tid) {
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X) + (size_t)r0 * ld, (short)0,
                                            0x7ffffff0, 0x00020000);
-    const int rsub = lane >> 3, c = (lane & 7) ^ rsub;
-    kc = c * EL::VEC;
     K = Kdim;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int row = 8 * (w * PER + i) + rsub;
-      voff[i] = (r0 + row < rlim) ? (uint32_t)(((size_t)row * ld + kc) * sizeof(S)) : OOB;
+      // lane l fills slot l % CPR of row l / CPR of this instruction's rows
+      const int row = Gm::RPI * (w * PER + i) + lane / Gm::CPR;
+      const int c = Gm::slot(row, lane % Gm::CPR);    // the chunk that belongs there
+      kc[i] = c * EL::VEC;
+      voff[i] = (r0 + row < rlim) ? (uint32_t)(((size_t)row * ld + kc[i]) * sizeof(S)) : OOB;
     }
   }
   __device__ __forceinline__ void issue(u32x4* stage, int k0) const {
     // the LDS destination (M0) must be wave-uniform: derive the wave id so the
     // compiler can see that
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t kbad = (k0 + kc < K) ? 0u : OOB;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t kbad = (k0 + kc[i] < K) ? 0u : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(stage + (w * PER + i) * 64), 16,
                                                (int)(voff[i] | kbad), k0 * (int)sizeof(S), 0, 0);
+    }
   }
 };
 
@@ -196,12 +216,12 @@ struct DmaK {
 // ROWS values of mn.  For bf16, 16-byte chunk c of k-row k sits at slot
 // c ^ ((k & 3) << 2): the transposed fragment reads below touch 4 consecutive
 // k-rows x 64 bytes per half wave, which this spreads over distinct banks.
-template <class EL, int ROWS, int THREADS>
+template <class EL, int ROWS, int THREADS, int BKB>
 struct DmaMN {
   typedef typename EL::storage S;
   static constexpr int V = EL::VEC;
   static constexpr int ROWB = ROWS * (int)sizeof(S);   // bytes per k-row
-  static constexpr int BK = 128 / (int)sizeof(S);       // k-rows per step
+  static constexpr int BK = BKB / (int)sizeof(S);       // k-rows per step
   static constexpr int INSTR = BK * ROWB / 1024;
   static constexpr int NW = THREADS / 64;
   static constexpr int PER = INSTR / NW;
@@ -240,17 +260,19 @@ struct DmaMN {
   }
 };
 
-// MFMA fragment of 32 mn-rows starting at r0, k sub-step s (16 k for bf16,
-// 8 k for fp32): lane l holds mn = r0 + (l & 31) and the 16-byte k-chunk
-// 2 s + (l >> 5).
-template <bool KMAJ, class EL, int ROWS>
+// MFMA fragment of 32 mn-rows starting at r0, k sub-step s of a step (16 k for
+// bf16, 8 k for fp32; BKB / 32 sub-steps): lane l holds mn = r0 + (l & 31) and
+// the 16-byte k-chunk 2 s + (l >> 5).
+template <bool KMAJ, class EL, int ROWS, int BKB>
 struct Frag;
 
-template <class EL, int ROWS>
-struct Frag<true, EL, ROWS> {
+template <class EL, int ROWS, int BKB>
+struct Frag<true, EL, ROWS, BKB> {
+  static constexpr int READS = 1;  // LDS read instructions per fragment
   __device__ __forceinline__ static u32x4 load(const u32x4* st, int r0, int s, int lane) {
+    typedef KGeom<BKB> Gm;
     const int row = r0 + (lane & 31), ch = 2 * s + (lane >> 5);
-    return st[row * 8 + (ch ^ (row & 7))];
+    return st[row * Gm::CPR + Gm::slot(row, ch)];
   }
 };
 
@@ -261,8 +283,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // lanes 4 q + i / 4, q = 0..3.  Lane j = 16 g + 4 q + r therefore addresses
 // k-row kb + q, mn columns mb + 4 r .. + 3, so that every lane i of the group
 // ends up with k = kb .. kb + 3 of mn = mb + i: half of its MFMA fragment.
-template <int ROWS>
-struct Frag<false, BF16, ROWS> {
+template <int ROWS, int BKB>
+struct Frag<false, BF16, ROWS, BKB> {
+  static constexpr int READS = 2;
   __device__ __forceinline__ static u32x4 load(const u32x4* st, int r0, int s, int lane) {
     constexpr int ROWB = ROWS * 2;
     const int g = lane >> 4, q = (lane >> 2) & 3, r = lane & 3;
@@ -286,8 +309,9 @@ struct Frag<false, BF16, ROWS> {
 
 // fp32 from a [k][mn] tile: the fp32 MFMA takes one value per lane, element q
 // of the lane's k-chunk, i.e. k = 4 (2 s + (l >> 5)) + q.
-template <int ROWS>
-struct Frag<false, F32, ROWS> {
+template <int ROWS, int BKB>
+struct Frag<false, F32, ROWS, BKB> {
+  static constexpr int READS = 4;
   __device__ __forceinline__ static u32x4 load(const u32x4* st, int r0, int s, int lane) {
     const float* base = reinterpret_cast<const float*>(st);
     const int col = r0 + (lane & 31), kb = 4 * (2 * s + (lane >> 5));
@@ -481,24 +505,75 @@ __device__ __forceinline__ void epi_srelu_bwd(const S* __restrict__ Hrow, S* __r
   }
 }
 
+// Workgroup barrier for the LDS ring.  __syncthreads() (and any fence whose
+// scope covers LDS) makes the compiler wait for every outstanding load first,
+// including the LDS-DMA loads of later ring stages, which would serialise the
+// pipeline.  Here each wave has already waited (vm_wait) for its loads into
+// the stage about to be read, and its reads of the stage about to be
+// overwritten have been consumed by MFMAs, so a bare s_barrier suffices; the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave are
+// outstanding (expcnt and lgkmcnt left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `ahead` whole steps (PERW loads each) are still in flight.
+template <int PERW, int MAXAHEAD>
+__device__ __forceinline__ void vm_wait_steps(int ahead) {
+  if constexpr (MAXAHEAD >= 2) {
+    if (ahead >= 2) {
+      vm_wait<2 * PERW>();
+      return;
+    }
+  }
+  if constexpr (MAXAHEAD >= 1) {
+    if (ahead >= 1) {
+      vm_wait<PERW>();
+      return;
+    }
+  }
+  vm_wait<0>();
+}
+
 // ------------------------------------------------------------------ the kernel
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, int BM, int BN, int WGM, int WGN>
+// Tile policy: block tile BM x BN, WGM x WGN waves, BKB bytes of K per pipeline
+// step, STAGES-deep LDS ring.
+// SCHED = 1 pins the k-step's instruction order: the first sub-step's fragment
+// reads, then one MFMA at a time with the next sub-step's reads spread between.
+template <int BM_, int BN_, int WGM_, int WGN_, int BKB_, int STAGES_, int SCHED_ = 0>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BKB = BKB_, STAGES = STAGES_;
+  static constexpr int SCHED = SCHED_;
+};
+
+template <class EL, int EPI, class TL>
 struct GemmCfg {
+  static constexpr int BM = TL::BM, BN = TL::BN, WGM = TL::WGM, WGN = TL::WGN;
   static constexpr int THREADS = WGM * WGN * 64;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int BK = 128 / sizeof(typename EL::storage);
-  static constexpr int GM = 8;  // M-tiles per band of the tile order
-  static constexpr size_t LDS_BYTES = 2 * (size_t)(BM + BN) * 128;
+  static constexpr int BKB = TL::BKB;
+  static constexpr int BK = BKB / sizeof(typename EL::storage);   // k per pipeline step
+  static constexpr int SUB = BKB / 32;                             // MFMA k sub-steps per step
+  static constexpr int STAGES = TL::STAGES;                        // LDS ring depth
+  static constexpr int STAGE_U4 = (BM + BN) * (BKB / 16);          // 16-byte units per stage
+  static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!epi_glu_fwd(EPI) || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
+  static_assert(LDS_BYTES + 8320 <= 160 * 1024, "LDS ring does not fit");
 };
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, int BM, int BN, int WGM, int WGN>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL>
+__global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     grouped_gemm_kernel(GemmArgs p) {
-  typedef GemmCfg<EL, AKM, BKM, GROUP, EPI, BM, BN, WGM, WGN> C;
+  typedef GemmCfg<EL, EPI, TL> C;
+  constexpr int BM = C::BM, BN = C::BN, WGN = C::WGN;
   typedef typename EL::storage S;
   constexpr int THREADS = C::THREADS, TM = C::TM, TN = C::TN, BK = C::BK;
   extern __shared__ u32x4 smem[];
@@ -564,18 +639,19 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
 
   const int G = gridDim.x;
   const int vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  u32x4* buf0 = smem;
-  u32x4* buf1 = smem + (BM + BN) * 8;
 
-  for (int tile = vb; tile < total; tile += G) {
-    // ---- decode the tile ----
+  // ---- tile decode: expert, row / column origin, row limit, k range ----
+  struct TileC {
     int e, m0, n0, mlim, kbeg, kend;
+  };
+  auto decode = [&](int tile) {
+    TileC t;
     if constexpr (GROUP == RAGGED_M) {
       const int total_m = s_tab[E];
-      const int span = C::GM * nN;
+      const int span = p.gm * nN;
       int band = tile / span, in = tile - band * span;
-      int first = band * C::GM;
-      int gsz = min(total_m - first, C::GM);
+      int first = band * p.gm;
+      int gsz = min(total_m - first, p.gm);
       int gm = first + in % gsz;
       int nt = in / gsz;
       int lo = 0, hi = E;
@@ -583,35 +659,76 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
         int mid = (lo + hi) >> 1;
         if (s_tab[mid] <= gm) lo = mid; else hi = mid;
       }
-      e = lo;
-      m0 = s_off[e] + (gm - s_tab[e]) * BM;
-      mlim = s_off[e + 1];
-      n0 = nt * BN;
-      kbeg = 0;
-      kend = p.K;
+      t.e = lo;
+      t.m0 = s_off[lo] + (gm - s_tab[lo]) * BM;
+      t.mlim = s_off[lo + 1];
+      t.n0 = nt * BN;
+      t.kbeg = 0;
+      t.kend = p.K;
     } else {
       const int per = mt_k * nt_k;
       int slot = tile / per, in = tile - slot * per;
-      e = s_tab[slot];
-      const int span = C::GM * nt_k;
+      t.e = s_tab[slot];
+      const int span = p.gm * nt_k;
       int band = in / span, r = in - band * span;
-      int first = band * C::GM;
-      int gsz = min(mt_k - first, C::GM);
-      m0 = (first + r % gsz) * BM;
-      n0 = (r / gsz) * BN;
-      mlim = p.M;
-      kbeg = s_off[e];
-      kend = max(s_off[e + 1], kbeg);
+      int first = band * p.gm;
+      int gsz = min(mt_k - first, p.gm);
+      t.m0 = (first + r % gsz) * BM;
+      t.n0 = (r / gsz) * BN;
+      t.mlim = p.M;
+      t.kbeg = s_off[t.e];
+      t.kend = max(s_off[t.e + 1], t.kbeg);
     }
+    // The coordinates come out of LDS tables but are the same on every lane:
+    // say so, so that addresses and buffer descriptors live in SGPRs.
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.mlim = __builtin_amdgcn_readfirstlane(t.mlim);
+    t.kbeg = __builtin_amdgcn_readfirstlane(t.kbeg);
+    t.kend = __builtin_amdgcn_readfirstlane(t.kend);
+    return t;
+  };
 
-    // The tile coordinates come out of LDS tables but are the same on every
-    // lane: say so, so that addresses and buffer descriptors live in SGPRs.
-    e = __builtin_amdgcn_readfirstlane(e);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    n0 = __builtin_amdgcn_readfirstlane(n0);
-    mlim = __builtin_amdgcn_readfirstlane(mlim);
-    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
-    kend = __builtin_amdgcn_readfirstlane(kend);
+  // Both operands go global -> LDS by DMA into a ring of STAGES buffers.
+  // Step kt waits until its own buffer has landed while the loads of the next
+  // STAGES - 2 steps stay in flight, meets the other waves at a barrier (after
+  // which nobody reads the buffer of step kt - 1 any more), refills that
+  // buffer with step kt + STAGES - 1, and runs the MFMAs of step kt.  (Issuing
+  // the next tile's first loads before the epilogue was measured: it gains
+  // nothing, and the ring position it needs costs more than that.)
+  constexpr int BKB = C::BKB, SUB = C::SUB, CPR = BKB / 16;
+  typedef typename std::conditional<AKM, DmaK<EL, BM, THREADS, BKB>,
+                                    DmaMN<EL, BM, THREADS, BKB>>::type LoadA;
+  typedef typename std::conditional<BKM, DmaK<EL, BN, THREADS, BKB>,
+                                    DmaMN<EL, BN, THREADS, BKB>>::type LoadB;
+  constexpr int S_ = C::STAGES;
+  constexpr int PERW = LoadA::PER + LoadB::PER;   // DMA instructions per wave per step
+  const S* A = reinterpret_cast<const S*>(p.a);
+  LoadA la;
+  LoadB lb;
+  auto stage_ptr = [&](int st) { return smem + (st % S_) * C::STAGE_U4; };
+  auto nk_of = [&](const TileC& t) { return (t.kend - t.kbeg + BK - 1) / BK; };
+  // set the loaders up for tile t and issue its first STAGES - 1 steps
+  auto prologue = [&](const TileC& t) {
+    const S* B = reinterpret_cast<const S*>(p.b);
+    if constexpr (GROUP == RAGGED_M) B += (size_t)t.e * p.b_expert_stride;
+    la.setup(A, p.lda, t.m0, t.mlim, t.kend, tid);
+    lb.setup(B, p.ldb, t.n0, p.N, t.kend, tid);
+    const int nk = nk_of(t);
+#pragma unroll
+    for (int st = 0; st < S_ - 1; ++st)
+      if (st < nk) {
+        la.issue(stage_ptr(st), t.kbeg + st * BK);
+        lb.issue(stage_ptr(st) + BM * CPR, t.kbeg + st * BK);
+      }
+  };
+
+  for (int tile = vb; tile < total; tile += G) {
+    const TileC cur = decode(tile);
+    const int nk = nk_of(cur);
+    __syncthreads();  // every wave is done with the previous tile's buffers
+    prologue(cur);
 
     // ---- main loop ----
     f32x16 acc[TM][TN];
@@ -622,61 +739,52 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const S* A = reinterpret_cast<const S*>(p.a);
-    const S* B = reinterpret_cast<const S*>(p.b);
-    if constexpr (GROUP == RAGGED_M) B += (size_t)e * p.b_expert_stride;
-    const int nk = (kend - kbeg + BK - 1) / BK;
-
-    // Both operands go global -> LDS by DMA; a step issues the loads of step
-    // kt + 1, runs the MFMAs of step kt, and ends with one barrier (which also
-    // waits for this wave's loads).
-    typedef typename std::conditional<AKM, DmaK<EL, BM, THREADS>, DmaMN<EL, BM, THREADS>>::type
-        LoadA;
-    typedef typename std::conditional<BKM, DmaK<EL, BN, THREADS>, DmaMN<EL, BN, THREADS>>::type
-        LoadB;
-    LoadA la;
-    LoadB lb;
-    la.setup(A, p.lda, m0, mlim, kend, tid);
-    lb.setup(B, p.ldb, n0, p.N, kend, tid);
-
-    if (nk > 0) {
-      __syncthreads();  // the previous tile's readers are done with buf0
-      la.issue(buf0, kbeg);
-      lb.issue(buf0 + BM * 8, kbeg);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        u32x4* cur = (kt & 1) ? buf1 : buf0;
-        u32x4* nxt = (kt & 1) ? buf0 : buf1;
-        if (kt + 1 < nk) {
-          la.issue(nxt, kbeg + (kt + 1) * BK);
-          lb.issue(nxt + BM * 8, kbeg + (kt + 1) * BK);
-        }
-        const u32x4* As = cur;
-        const u32x4* Bs = cur + BM * 8;
-        // fragments of sub-step s + 1 are read while the MFMAs of s run
-        u32x4 af[2][TM], bfr[2][TN];
+    for (int kt = 0; kt < nk; ++kt) {
+      // loads issued after step kt's: steps kt+1 .. min(kt+S-2, nk-1)
+      vm_wait_steps<PERW, S_ - 2>(min(S_ - 2, nk - 1 - kt));
+      lds_barrier();
+      if (kt + S_ - 1 < nk) {
+        u32x4* nb = stage_ptr(kt + S_ - 1);
+        la.issue(nb, cur.kbeg + (kt + S_ - 1) * BK);
+        lb.issue(nb + BM * CPR, cur.kbeg + (kt + S_ - 1) * BK);
+      }
+      const u32x4* As = stage_ptr(kt);
+      const u32x4* Bs = As + BM * CPR;
+      // fragments of sub-step s + 1 are read while the MFMAs of s run;
+      // read in order of first use by the i-major MFMA loop: a0, b0 .. b(TN-1), a1 ..
+      u32x4 af[2][TM], bfr[2][TN];
+      auto frags = [&](int buf, int s2) {
+        af[buf][0] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM, s2, lane);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[0][i] = Frag<AKM, EL, BM>::load(As, wm * C::WTM + 32 * i, 0, lane);
+        for (int j = 0; j < TN; ++j)
+          bfr[buf][j] = Frag<BKM, EL, BN, BKB>::load(Bs, wn * C::WTN + 32 * j, s2, lane);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[0][j] = Frag<BKM, EL, BN>::load(Bs, wn * C::WTN + 32 * j, 0, lane);
+        for (int i = 1; i < TM; ++i)
+          af[buf][i] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM + 32 * i, s2, lane);
+      };
+      frags(0, 0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s < 3) {
+      for (int s2 = 0; s2 < SUB; ++s2) {
+        if (s2 + 1 < SUB) frags((s2 + 1) & 1, s2 + 1);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-              af[(s + 1) & 1][i] = Frag<AKM, EL, BM>::load(As, wm * C::WTM + 32 * i, s + 1, lane);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              bfr[(s + 1) & 1][j] = Frag<BKM, EL, BN>::load(Bs, wn * C::WTN + 32 * j, s + 1, lane);
-          }
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) mma(acc[i][j], bfr[s & 1][j], af[s & 1][i], EL());
-        }
-        __syncthreads();
+          for (int j = 0; j < TN; ++j) mma(acc[i][j], bfr[s2 & 1][j], af[s2 & 1][i], EL());
+      }
+      if constexpr (TL::SCHED == 1) {
+        constexpr int NR = TM * Frag<AKM, EL, BM, BKB>::READS + TN * Frag<BKM, EL, BN, BKB>::READS;
+        constexpr int NM = TM * TN;
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        static_for<0, SUB>([&](auto s2) {
+          static_for<0, NM>([&](auto m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            constexpr int nr = (NR * (m + 1)) / NM - (NR * m) / NM;
+            if constexpr (s2 + 1 < SUB && nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+          });
+        });
       }
     }
+    const int e = cur.e, m0 = cur.m0, n0 = cur.n0, mlim = cur.mlim;
 
     // ---- epilogue: lane holds rows (lane & 31) + 32 i, columns 32 j + 8 g + 4 h + q ----
     const int cw = n0 + wn * C::WTN + 4 * (lane >> 5);  // column of the lane's first value
@@ -724,10 +832,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
 
 // ------------------------------------------------------------------ launching
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, int BM, int BN, int WGM, int WGN>
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL>
 moe_status_t launch_gemm(const GemmArgs& p, int max_cus, hipStream_t s) {
-  typedef GemmCfg<EL, AKM, BKM, GROUP, EPI, BM, BN, WGM, WGN> C;
-  auto kern = grouped_gemm_kernel<EL, AKM, BKM, GROUP, EPI, BM, BN, WGM, WGN>;
+  typedef GemmCfg<EL, EPI, TL> C;
+  auto kern = grouped_gemm_kernel<EL, AKM, BKM, GROUP, EPI, TL>;
   static int occ[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
@@ -751,39 +859,62 @@ moe_status_t launch_gemm(const GemmArgs& p, int max_cus, hipStream_t s) {
   return launch_status();
 }
 
-// Tile shapes: large problems take 256 x 256 tiles (4 waves of 128 x 128),
-// small or narrow ones 128 x 128 (4 waves of 64 x 64).  fp32 takes 64 x 128.
+// Tile policies.  Large bf16 problems take 256 x 256 tiles with a two-stage
+// ring of 128-byte k-steps (64 KB each) and the pinned MFMA / LDS-read
+// interleave: 16 waves in a 4 x 4 grid (64 x 64 per wave) for the plain
+// epilogue, 8 waves in 2 x 4 (128 x 64 per wave) for the gated epilogues,
+// whose extra registers do not fit under the 16-wave limit of 128 VGPRs.
+// Small or narrow problems take 128 x 128, fp32 takes 64 x 128.
+// MOE_GEMM_TILE=<n> in the environment selects variant n of the list below
+// for bf16 instead (tuning sweeps).
+typedef Tile<256, 256, 4, 4, 128, 2, 1> TBig;
+typedef Tile<256, 256, 2, 4, 128, 2, 1> TBigGlu;
+typedef Tile<128, 128, 2, 2, 128, 2> TSmall;
+typedef Tile<64, 128, 2, 2, 128, 2> TF32;
+
+inline int tile_variant() {
+  const char* v = getenv("MOE_GEMM_TILE");
+  return v ? atoi(v) : -1;
+}
+
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI>
 moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
   if constexpr (sizeof(typename EL::storage) == 4) {
-    return launch_gemm<EL, AKM, BKM, GROUP, EPI, 64, 128, 2, 2>(p, max_cus, s);
+    return launch_gemm<EL, AKM, BKM, GROUP, EPI, TF32>(p, max_cus, s);
   } else {
-    if (big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, 256, 256, 2, 2>(p, max_cus, s);
-    return launch_gemm<EL, AKM, BKM, GROUP, EPI, 128, 128, 2, 2>(p, max_cus, s);
+    constexpr bool kSweep = (EPI == EPI_STORE || EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
+    if constexpr (kSweep) {
+      switch (tile_variant()) {
+        case 0: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig>(p, max_cus, s);
+        case 1: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu>(p, max_cus, s);
+        case 2: return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 4, 4, 128, 2, 0>>(p, max_cus, s);
+        case 3: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall>(p, max_cus, s);
+        default: break;
+      }
+    }
+    if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall>(p, max_cus, s);
+    if constexpr (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))
+      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu>(p, max_cus, s);
+    else return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig>(p, max_cus, s);
   }
-}
-
-// MOE_GEMM_TILE=128 or 256 in the environment overrides the tile-shape choice
-// (for tuning and for testing both shapes on small problems).
-inline bool tile_override(bool big) {
-  const char* v = getenv("MOE_GEMM_TILE");
-  if (!v) return big;
-  if (v[0] == '1') return false;
-  if (v[0] == '2') return true;
-  return big;
 }
 
 template <bool AKM, bool BKM, int GROUP, int EPI>
 moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
-  big = tile_override(big);
   if (dtype == MOE_BF16) return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
   return dispatch_tiles<F32, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
 }
 
+// MOE_GEMM_GM in the environment overrides the band height (for tuning).
 inline GemmArgs zero_args() {
   GemmArgs p;
   memset(&p, 0, sizeof(p));
   p.alpha = 1.0f;
+  p.gm = 8;
+  if (const char* v = getenv("MOE_GEMM_GM")) {
+    int g = atoi(v);
+    if (g >= 1 && g <= 64) p.gm = g;
+  }
   return p;
 }
 
