@@ -52,6 +52,14 @@ Readings of points the pages leave open (each is listed in the design doc):
    gradient passes where the raw value lies inside the closed interval.
  * alpha scales the sigmoid argument: silu_a(g) = g * sigmoid(a g).
  * b2 is added to each expert output before the gate weighting.
+ * MXFP8 operands ([P1 Quant]; format in ``oracle/mx.py``): every GEMM operand
+   is quantized in blocks of 32 along that GEMM's reduction axis.  Row copies
+   (blocks along features) feed the forward and dgrad GEMMs; column copies
+   (blocks along tokens, anchored at each expert's segment start, the last
+   block zero-padded) feed the weight gradients.  A and dH are quantized from
+   their exact epilogue values, Xp from the stored x, dY from the product
+   w * dOut; H stays a bf16 tensor for the backward epilogue.  Biases are not
+   part of the MXFP8 variant.
 """
 from __future__ import annotations
 
@@ -59,6 +67,8 @@ import math
 from typing import Optional
 
 import numpy as np
+
+from . import mx as _mx
 
 # ---------------------------------------------------------------------------
 # Storage rounding
@@ -478,7 +488,7 @@ class LayerSpec:
     """Options of the layer (what the configs vary)."""
 
     def __init__(self, k, score="softmax", normalize=True, act="swiglu", clamp=0.0,
-                 alpha=1.0, gelu_tanh=False, store="bf16"):
+                 alpha=1.0, gelu_tanh=False, store="bf16", gemm="bf16"):
         self.k = k
         self.score = score
         self.normalize = normalize
@@ -487,10 +497,15 @@ class LayerSpec:
         self.alpha = alpha
         self.gelu_tanh = gelu_tanh
         self.store = store      # dtype of every stored activation: "bf16", "f32" or "f64"
+        self.gemm = gemm        # GEMM operands: "bf16"/"f32" (the stored tensors) or "mxfp8"
 
     @property
     def gated(self):
         return self.act in ("swiglu", "geglu")
+
+    @property
+    def mx(self):
+        return self.gemm == "mxfp8"
 
 
 def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
@@ -506,19 +521,36 @@ def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
     idx, w, nan = route_topk(logits, spec.k, spec.score, spec.normalize)
     counts, offsets, row_map, src_row = permute_indices(idx, E)
     xp = gather_rows(_f64(x), src_row)
-    H = grouped_linear(xp, W1, offsets, b1)
+    q = spec.mx
+    if q and (b1 is not None or b2 is not None):
+        raise ValueError("the MXFP8 variant has no biases")
+    pad = pad_offsets(counts) if q else None
+    # FC1 reduces over d: activations and weights blocked along d
+    H = grouped_linear(_mx.mx_qdq(xp, 1) if q else xp, _mx.mx_qdq(_f64(W1), 2) if q else W1,
+                       offsets, b1)
     if spec.gated:
         f = W1.shape[1] // 2
         A = glu_forward(H[:, :f], H[:, f:], spec.act, spec.clamp, spec.alpha, spec.gelu_tanh)
     else:
         A = srelu_forward(H, spec.clamp)
-    H_s, A_s = rnd(H), rnd(A)
-    Y = grouped_linear(A_s, W2, offsets, b2)
+    H_s = rnd(H)
+    res = {}
+    if q:
+        # A from its exact values: row copy along f for FC2, column copy along
+        # tokens for the FC2 weight gradient
+        A_fc2 = _mx.mx_qdq(A, 1)
+        res.update(A_row=A_fc2, A_col=_mx.mx_qdq_segments_colwise(A, offsets, pad),
+                   xp_col=_mx.mx_qdq_segments_colwise(xp, offsets, pad), pad_offsets=pad)
+        A_s = A_fc2
+    else:
+        A_s = A_fc2 = rnd(A)
+    Y = grouped_linear(A_fc2, _mx.mx_qdq(_f64(W2), 2) if q else W2, offsets, b2)
     Y_s = rnd(Y)
     out = combine(Y_s, row_map, w)
-    return dict(topk_idx=idx, topk_w=w, nan=nan, counts=counts, offsets=offsets,
-                row_map=row_map, src_row=src_row, xp=xp, H=H_s, A=A_s, Y=Y_s,
-                out=rnd(out), H_exact=H, A_exact=A, Y_exact=Y, out_exact=out)
+    res.update(topk_idx=idx, topk_w=w, nan=nan, counts=counts, offsets=offsets,
+               row_map=row_map, src_row=src_row, xp=xp, H=H_s, A=A_s, Y=Y_s,
+               out=rnd(out), H_exact=H, A_exact=A, Y_exact=Y, out_exact=out)
+    return res
 
 
 def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias=False):
@@ -527,12 +559,22 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
     ``spec.store`` and the weight / bias / gate gradients kept in float64."""
     rnd = storage_round(spec.store)
     offsets, row_map = fwd["offsets"], fwd["row_map"]
+    q = spec.mx
     dout = _f64(dout)
     dY, dgate = combine_bwd(dout, fwd["Y"], row_map, fwd["topk_w"])
-    dY_s = rnd(dY)
     dlogits = route_topk_bwd(logits, fwd["topk_idx"], dgate, spec.score, spec.normalize)
-    dW2, db2 = grouped_wgrad(dY_s, fwd["A"], offsets, with_bias=True)
-    dA = grouped_dgrad(dY_s, W2, offsets)
+    if q:
+        pad = fwd["pad_offsets"]
+        # dY from the product w * dOut: row copy along d (FC2 dgrad), column
+        # copy along tokens (FC2 weight gradient); W2 blocked along d
+        dY_s = _mx.mx_qdq(dY, 1)
+        dY_col = _mx.mx_qdq_segments_colwise(dY, offsets, pad)
+        dW2, db2 = grouped_wgrad(dY_col, fwd["A_col"], offsets, with_bias=True)
+        dA = grouped_dgrad(dY_s, _mx.mx_qdq(_f64(W2), 1), offsets)
+    else:
+        dY_s = rnd(dY)
+        dW2, db2 = grouped_wgrad(dY_s, fwd["A"], offsets, with_bias=True)
+        dA = grouped_dgrad(dY_s, W2, offsets)
     H = fwd["H"]
     if spec.gated:
         f = W1.shape[1] // 2
@@ -541,13 +583,25 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
         dH = np.concatenate([dg, dl], axis=1)
     else:
         dH = srelu_backward(dA, H, spec.clamp)
-    dH_s = rnd(dH)
-    dW1, db1 = grouped_wgrad(dH_s, fwd["xp"], offsets, with_bias=True)
-    dXp = grouped_dgrad(dH_s, W1, offsets)
+    if q:
+        # dH from its exact values: row copy along 2f (FC1 dgrad; with f a
+        # multiple of 32 its blocks are the same in packed and canonical
+        # order), column copy along tokens (FC1 weight gradient); W1 blocked
+        # along 2f for the dgrad
+        dH_s = _mx.mx_qdq(dH, 1)
+        dH_col = _mx.mx_qdq_segments_colwise(dH, offsets, pad)
+        dW1, db1 = grouped_wgrad(dH_col, fwd["xp_col"], offsets, with_bias=True)
+        dXp = grouped_dgrad(dH_s, _mx.mx_qdq(_f64(W1), 1), offsets)
+    else:
+        dH_s = rnd(dH)
+        dW1, db1 = grouped_wgrad(dH_s, fwd["xp"], offsets, with_bias=True)
+        dXp = grouped_dgrad(dH_s, W1, offsets)
     dXp_s = rnd(dXp)
     dX = combine(dXp_s, row_map, None)
     out = dict(dY=dY_s, dgate=dgate, dlogits=dlogits, dA=dA, dH=dH_s, dW2=dW2, dXp=dXp_s,
                dW1=dW1, dX=rnd(dX), dY_exact=dY, dH_exact=dH, dXp_exact=dXp, dX_exact=dX)
+    if q:
+        out.update(dY_col=dY_col, dH_col=dH_col)
     if has_bias:
         out["db1"] = db1
         out["db2"] = db2
