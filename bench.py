@@ -24,6 +24,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2        # MI355X dense fp8 MFMA (MXFP8 operands)
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE FFN fwd+bwd TFLOPS and % of MFMA peak, 1×MI355X"
@@ -65,7 +66,15 @@ def hbm_bytes(cfg):
     out = {"route_topk": T * E * 4 + T * k * 8,
            "permute": T * d * b + R * d * b + T * k * 4 + 8 * R,
            "combine": R * d * b + T * d * b + 8 * R}
+    if cfg.gemm == "mxfp8":
+        # MXFP8 copies of Xp and dY, written straight from x / d_out: the rows
+        # are gathered once per copy (row and segment-column), codes + scales out
+        mxb = lambda n: R * n + R * n // 32
+        out["permute"] = T * k * 4 + 12 * R
+        out["quantize_x"] = 2 * R * d * b + 2 * mxb(d)
     if cfg.backward:
+        if cfg.gemm == "mxfp8":
+            out["quantize_dy"] = 2 * R * d * b + 2 * mxb(d) + 8 * R
         out.update({"combine_bwd": T * d * b + 2 * R * d * b + 12 * R,
                     "route_topk_bwd": T * E * 8 + T * k * 8,
                     "unpermute_dx": R * d * b + T * d * b + 4 * R})
@@ -110,7 +119,7 @@ def cpu_baseline(cfg, inp, tokens):
     b1 = inp.get("b1") if cfg.bias else None
     b2 = inp.get("b2") if cfg.bias else None
     spec = om.LayerSpec(cfg.k, cfg.score, cfg.normalize, cfg.act, cfg.clamp, cfg.alpha,
-                        store=cfg.dtype)
+                        store=cfg.dtype, gemm=cfg.gemm)
     t0 = time.perf_counter()
     fwd = om.layer_forward(x, lg, W1, W2, b1, b2, spec=spec)
     if cfg.backward:
@@ -120,7 +129,8 @@ def cpu_baseline(cfg, inp, tokens):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"first {Tc} of {cfg.T} tokens of {cfg.name} (R={Tc * cfg.k} routed rows), "
-                      f"full expert weights, forward{'+backward' if cfg.backward else ''}, fp64"}
+                      f"full expert weights, forward{'+backward' if cfg.backward else ''}, fp64"
+                      + (", MXFP8 QDQ of every GEMM operand" if cfg.gemm == "mxfp8" else "")}
 
 
 def main():
@@ -163,9 +173,15 @@ def main():
     else:
         W1p, b1p = W1, b1
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    mx = cfg.gemm == "mxfp8"
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-               backward=cfg.backward)
+               backward=cfg.backward, gemm=cfg.gemm)
+    if mx:
+        # the MXFP8 weight copies are made once, outside the timed steps (the
+        # weights do not change between the synthetic steps)
+        W1p = MoEFFN.mx_weights(W1p, W2)
+        W2 = None
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -201,7 +217,8 @@ def main():
         kernels[name] = row
     gemm_ms = sum(per_op[n][1] for n in flops)
     dom = max(flops, key=lambda n: per_op[n][1])
-    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    peak = (PEAK_F32_TFLOPS if cfg.dtype == "f32" else
+            PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS)
     achieved = flops[dom] / per_op[dom][1] / 1e9
     value = total_flops / ms_step / 1e9
 
@@ -225,7 +242,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if cfg.dtype == "f32" else "bf16", "data": "synthetic",
+        "dtype": "f32" if cfg.dtype == "f32" else ("mxfp8" if mx else "bf16"), "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "k": cfg.k, "routed_rows": cfg.R, "score": cfg.score, "act": cfg.act,
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},

@@ -68,7 +68,19 @@ typedef enum {
   MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_E4M3 = 2  /* MXFP8 GEMM operands (moe_mx_t); see the MXFP8 section below */
+} moe_dtype_t;
+
+/* An MXFP8 matrix (layout and format in the MXFP8 section below). */
+typedef struct {
+  uint8_t* data;   /* E4M3 codes [rows, ld] */
+  uint8_t* scale;  /* E8M0 codes [rows, ld / 32] */
+  int64_t ld;      /* elements per row, a multiple of 32 */
+} moe_mx_t;
+
 
 typedef enum {
   MOE_ACT_SWIGLU = 0,  /* silu_a(gate) * lin,  silu_a(g) = g * sigmoid(a g)   */
@@ -188,6 +200,16 @@ typedef struct {
   void* h_out;
   void* a_out;
   int max_cus;
+  /* dtype == MOE_E4M3: xp_mx [R, d] and w1_mx [E*n1, d] (row copies along
+   * d) replace xp / w1p; h_out stays bf16; A is written as a_row (row copy
+   * [R, f], nullable) and a_col (column copy [f, moe_mx_col_len], nullable,
+   * needs pad_offsets), quantized from the float32 epilogue values.  Gated
+   * activations only, no bias. */
+  const moe_mx_t* xp_mx;
+  const moe_mx_t* w1_mx;
+  moe_mx_t* a_row;
+  moe_mx_t* a_col;
+  const int32_t* pad_offsets;
 } moe_glu_fwd_args_t;
 moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* args, void* stream);
 
@@ -204,6 +226,10 @@ typedef struct {
   int E, R, N, K;
   void* y;
   int max_cus;
+  /* dtype == MOE_E4M3: a_mx [R, K] and w_mx [E*N, K] row copies replace a / w;
+   * y is bf16; no bias. */
+  const moe_mx_t* a_mx;
+  const moe_mx_t* w_mx;
 } moe_gemm_fwd_args_t;
 moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* args, void* stream);
 
@@ -228,6 +254,16 @@ typedef struct {
   int gelu_tanh;
   void* dh;
   int max_cus;
+  /* dtype == MOE_E4M3: dy_mx [R, d] (row copy along d) and w2t_mx [E*f, d]
+   * (W2 transposed, blocked along d) replace dy / w2; h is bf16; dH is written
+   * as dh_row (row copy [R, n1] in the packed layout, nullable) and dh_col
+   * (column copy [n1, moe_mx_col_len], nullable, needs pad_offsets), quantized
+   * from the float32 epilogue values.  Gated activations only. */
+  const moe_mx_t* dy_mx;
+  const moe_mx_t* w2t_mx;
+  moe_mx_t* dh_row;
+  moe_mx_t* dh_col;
+  const int32_t* pad_offsets;
 } moe_glu_bwd_args_t;
 moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* args, void* stream);
 
@@ -251,8 +287,74 @@ typedef struct {
   float* db;           /* WGRAD, nullable */
   int accumulate;
   int max_cus;
+  /* dtype == MOE_E4M3:
+   *   DGRAD: g_mx [R, N] row copy, w_mx [E*K, N] (w transposed, blocked along
+   *          N); da is bf16.
+   *   WGRAD: g_mx [N, L] and a_mx [K, L] column copies (L = moe_mx_col_len),
+   *          segments from pad_offsets; dw float32; db must be NULL. */
+  const moe_mx_t* g_mx;
+  const moe_mx_t* a_mx;
+  const moe_mx_t* w_mx;
+  const int32_t* pad_offsets;
 } moe_gemm_bwd_args_t;
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream);
+
+/* ---------------------------------------------------------------- MXFP8 (a14)
+ * [P1] section "MXFP8 および NVFP4 量子化の融合による露出メモリオーバーヘッドの削減":
+ * GEMM outputs are quantized to MXFP8 inside the kernels that produce them,
+ * together with a transposed copy for the backward pass, so quantization
+ * costs no separate pass over memory.  Format: OCP Microscaling Formats (MX)
+ * v1.0 -- E4M3 elements (largest magnitude 448, no infinities) and one E8M0
+ * scale 2^(code - 127) per 32 consecutive elements of a row; a block with
+ * largest magnitude amax has shared exponent e = floor(log2 amax) - 8,
+ * clamped to [-127, 127] (amax = 0: e = -127), and elements
+ * round_to_nearest_even(v / 2^e) saturated to +-448.
+ *
+ * A quantized matrix is a moe_mx_t: `data` [rows, ld] E4M3 codes, `scale`
+ * [rows, ld / 32] E8M0 codes (scale[r * ld/32 + b] covers data[r*ld + 32b ..
+ * 32b + 31]), ld a multiple of 32.  Every GEMM operand is blocked along that
+ * GEMM's reduction axis, so each operand is a K-contiguous MX matrix:
+ *  - row copy of X [R, n]: rows = R, ld = n (blocks along the features);
+ *  - column copy of X [R, n] split into expert segments: rows = n, ld =
+ *    moe_mx_col_len(R, E); expert e's tokens occupy [pad_offsets[e],
+ *    pad_offsets[e+1]) of every row (the segment start anchors the 32-blocks,
+ *    the tail of the last block is zero); entries past pad_offsets[E] are not
+ *    written;
+ *  - weight copies: W [E, N, K] blocked along K is a row copy with rows E*N,
+ *    ld = K; blocked along N it is the transposed copy [E*K rows, ld = N].
+ * MX GEMM operands need the reduction length (K, ld) a multiple of 128.
+ * The layer's MXFP8 variant has no biases.  (moe_mx_t is declared beside the
+ * element types above.) */
+
+/* Length of the token axis of an expert-segmented column copy:
+ * R + 31 E rounded up to a multiple of 128 (an upper bound of pad_offsets[E]). */
+int64_t moe_mx_col_len(int R, int E);
+
+/* Row copy: out = MX(x) along the last axis.  x [rows, n] dtype (F32 or BF16),
+ * n a multiple of 32; out->data [rows, out->ld >= n], blocks along n. */
+moe_status_t moe_mx_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
+                             void* stream);
+
+/* Transposed copy of a batch of matrices: x [batches, rows, n] dtype, rows a
+ * multiple of 32; out row b*n + c holds column c of matrix b, blocked along
+ * rows: out->data [batches * n, out->ld >= rows]. */
+moe_status_t moe_mx_quantize_transpose(const void* x, int dtype, int batches, int rows, int n,
+                                       moe_mx_t* out, void* stream);
+
+/* Row and/or column copies of an expert-ordered tensor, read straight from
+ * its source rows (a2 and a6 fused with the quantization):
+ *   v[r][c] = x[src_row ? src_row[r] : r][c] * (topk_w ? topk_w[t*k + j] : 1)
+ * where t = src_row[r] and row_map[t*k + j] = r (float32 product).  With
+ * src_row = x's permutation this is Xp; with x = d_out and the gates it is
+ * dY = w * dOut.  x [*, n] dtype; src_row, offsets, pad_offsets from
+ * moe_permute; row_map and topk_w required together, and only with src_row.
+ *   row_out (nullable): [R, ld >= n] blocks along n;
+ *   col_out (nullable): [n, moe_mx_col_len(R, E)] blocks along tokens. */
+moe_status_t moe_mx_quantize_experts(const void* x, int dtype, const int32_t* src_row,
+                                     const int32_t* row_map, const float* topk_w, int k,
+                                     const int32_t* offsets, const int32_t* pad_offsets, int E,
+                                     int R, int n, moe_mx_t* row_out, moe_mx_t* col_out,
+                                     void* stream);
 
 /* ---------------------------------------------------------------- combine
  * a5 / a12.  out[t] = sum_{j=0..k-1} topk_w[t,j] * y[row_map[t,j]], summed in
@@ -265,7 +367,8 @@ moe_status_t moe_unpermute_combine(const void* y, int dtype, const int32_t* row_
 /* a6.  Backward of the combine:
  *   d_y[row_map[t,j]]  = topk_w[t,j] * d_out[t]        (dtype, rounded once)
  *   d_topk_w[t,j]      = <d_out[t], y[row_map[t,j]]>   (float32)
- * d_out [T, d], y [T*k, d], d_y [T*k, d] dtype. */
+ * d_out [T, d], y [T*k, d], d_y [T*k, d] dtype.  d_y or d_topk_w may be NULL
+ * (an MXFP8 layer writes dY only as MXFP8 copies, with moe_mx_quantize_experts). */
 moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dtype,
                                        const int32_t* row_map, const float* topk_w, int T,
                                        int k, int d, void* d_y, float* d_topk_w, void* stream);

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 ACT = {"swiglu": 0, "geglu": 1, "srelu": 2}
 SCORE = {"softmax": 0, "sigmoid": 1}
 MOE_BWD_DGRAD, MOE_BWD_WGRAD = 0, 1
@@ -23,18 +23,28 @@ ERRBIT_NAN_LOGIT, ERRBIT_BAD_EXPERT = 1, 2
 c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
 
+class MxT(ctypes.Structure):
+    """moe_mx_t: E4M3 codes [rows, ld], E8M0 scales [rows, ld / 32]."""
+    _fields_ = [("data", c_void_p), ("scale", c_void_p), ("ld", ctypes.c_int64)]
+
+
+_PMX = ctypes.POINTER(MxT)
+
+
 class GluFwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("xp", c_void_p), ("w1p", c_void_p),
                 ("b1p", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
                 ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
                 ("alpha", c_float), ("gelu_tanh", c_int), ("h_out", c_void_p),
-                ("a_out", c_void_p), ("max_cus", c_int)]
+                ("a_out", c_void_p), ("max_cus", c_int), ("xp_mx", _PMX), ("w1_mx", _PMX),
+                ("a_row", _PMX), ("a_col", _PMX), ("pad_offsets", c_void_p)]
 
 
 class GemmFwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("a", c_void_p), ("w", c_void_p),
                 ("b", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
-                ("N", c_int), ("K", c_int), ("y", c_void_p), ("max_cus", c_int)]
+                ("N", c_int), ("K", c_int), ("y", c_void_p), ("max_cus", c_int),
+                ("a_mx", _PMX), ("w_mx", _PMX)]
 
 
 class GluBwdArgs(ctypes.Structure):
@@ -42,14 +52,16 @@ class GluBwdArgs(ctypes.Structure):
                 ("h", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
                 ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
                 ("alpha", c_float), ("gelu_tanh", c_int), ("dh", c_void_p),
-                ("max_cus", c_int)]
+                ("max_cus", c_int), ("dy_mx", _PMX), ("w2t_mx", _PMX), ("dh_row", _PMX),
+                ("dh_col", _PMX), ("pad_offsets", c_void_p)]
 
 
 class GemmBwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("mode", c_int), ("g", c_void_p),
                 ("a", c_void_p), ("w", c_void_p), ("offsets", c_void_p), ("E", c_int),
                 ("R", c_int), ("N", c_int), ("K", c_int), ("out", c_void_p), ("db", c_void_p),
-                ("accumulate", c_int), ("max_cus", c_int)]
+                ("accumulate", c_int), ("max_cus", c_int), ("g_mx", _PMX), ("a_mx", _PMX),
+                ("w_mx", _PMX), ("pad_offsets", c_void_p)]
 
 
 _SIGS = {
@@ -74,6 +86,12 @@ _SIGS = {
                                       c_void_p, c_void_p]),
     "moe_unpermute_combine_bwd": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int,
                                           c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "moe_mx_col_len": (ctypes.c_int64, [c_int, c_int]),
+    "moe_mx_quantize": (c_int, [c_void_p, c_int, ctypes.c_int64, c_int, _PMX, c_void_p]),
+    "moe_mx_quantize_transpose": (c_int, [c_void_p, c_int, c_int, c_int, c_int, _PMX, c_void_p]),
+    "moe_mx_quantize_experts": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                        c_void_p, c_void_p, c_int, c_int, c_int, _PMX, _PMX,
+                                        c_void_p]),
 }
 
 _lib = None

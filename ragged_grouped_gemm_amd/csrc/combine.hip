@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
         part = fmaf(g[q], v[q], part);
         o[q] = wj * g[q];
       }
-      dy[(size_t)r * chunks + c] = pack_chunk(o, EL());
+      if (dy) dy[(size_t)r * chunks + c] = pack_chunk(o, EL());
     }
     float tot = wave_sum(part);
     if (lane == 0 && dw) dw[(size_t)t * k + j] = tot;
@@ -169,7 +169,7 @@ moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dty
                                        int k, int d, void* d_y, float* d_topk_w, void* stream) {
   MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && d > 0 && valid_dtype(dtype));
   if (T == 0) return MOE_OK;
-  MOE_CHECK_ARG(d_out && y && row_map && topk_w && d_y);
+  MOE_CHECK_ARG(d_out && y && row_map && topk_w && (d_y || d_topk_w));
   MOE_CHECK_ARG(aligned16(d_out) && aligned16(y) && aligned16(d_y));
   MOE_CHECK_ARG((d * dtype_size(dtype)) % 16 == 0);
   int chunks = (int)(d * dtype_size(dtype) / 16);

@@ -37,8 +37,10 @@
 //    row: the epilogue writes 8- or 16-byte vectors, and the gate and linear
 //    halves of a GLU pair sit in the same lane at the same positions.
 #include "common.hpp"
+#include "mx.hpp"
 
 #include <math.h>
+#include <stddef.h>
 #include <stdlib.h>
 
 #include <type_traits>
@@ -60,6 +62,28 @@ constexpr bool epi_glu_fwd(int e) { return e == EPI_SWIGLU_FWD || e == EPI_GEGLU
 constexpr bool epi_glu_bwd(int e) { return e == EPI_SWIGLU_BWD || e == EPI_GEGLU_BWD; }
 enum { RAGGED_M = 0, RAGGED_K = 1 };
 
+// MXFP8 operands: E4M3 codes (16 per 16-byte chunk) with one E8M0 scale per
+// 32 along K, multiplied by v_mfma_scale_f32_32x32x64_f8f6f4.  Both operands
+// are K-contiguous; outputs of these GEMMs are bf16 (or float32 for weight
+// gradients, or MXFP8 copies written by the epilogue).
+struct MX8 {
+  typedef uint8_t storage;
+  static constexpr int VEC = 16;
+};
+template <class EL>
+constexpr bool is_mx() {
+  return std::is_same<EL, MX8>::value;
+}
+// storage type of the GEMM's own outputs (C, saved H)
+template <class EL>
+struct OutT {
+  typedef typename EL::storage type;
+};
+template <>
+struct OutT<MX8> {
+  typedef uint16_t type;
+};
+
 struct GemmArgs {
   const void* a;
   const void* b;
@@ -77,6 +101,20 @@ struct GemmArgs {
   int act, gelu_tanh;
   int accumulate;
   int gm;  // M-tiles per band of the tile order
+  // MXFP8 operands (MX8): E8M0 scales of A and B, row strides in bytes
+  const uint8_t* sa;
+  const uint8_t* sb;
+  long long slda, sldb;
+  long long sb_expert_stride;  // RAGGED_M: bytes between experts' B scales
+  // MXFP8 copies of the epilogue's output (A of FC1, dH of the dGLU):
+  // row copy [R, ld_mxr] and expert-segmented column copy [n, ld_mxc]
+  uint8_t* mxr;
+  uint8_t* mxr_s;
+  long long ld_mxr;
+  uint8_t* mxc;
+  uint8_t* mxc_s;
+  long long ld_mxc;
+  const int32_t* pad_offsets;
 };
 
 // ------------------------------------------------------------------ activations
@@ -182,14 +220,15 @@ struct DmaK {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff[PER];
   int kc[PER];
-  int K;
+  int K, Klo;
 
   __device__ __forceinline__ void setup(const S* X, long long ld, int r0, int rlim, int Kdim,
-                                        int tid) {
+                                        int tid, int Kmin = 0) {
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X) + (size_t)r0 * ld, (short)0,
                                            0x7ffffff0, 0x00020000);
     K = Kdim;
+    Klo = Kmin;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       // lane l fills slot l % CPR of row l / CPR of this instruction's rows
@@ -205,7 +244,8 @@ struct DmaK {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t kbad = (k0 + kc[i] < K) ? 0u : OOB;
+      const int kk = k0 + kc[i];
+      const uint32_t kbad = (kk < K && kk >= Klo) ? 0u : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(stage + (w * PER + i) * 64), 16,
                                                (int)(voff[i] | kbad), k0 * (int)sizeof(S), 0, 0);
     }
@@ -234,7 +274,7 @@ struct DmaMN {
   int c0, clim, kend, krl, slot;
 
   __device__ __forceinline__ void setup(const S* X_, long long ld_, int c0_, int clim_, int kend_,
-                                        int tid) {
+                                        int tid, int /*Kmin: every step starts in range*/ = 0) {
     X = X_;
     ld = ld_;
     c0 = c0_;
@@ -322,6 +362,60 @@ struct Frag<false, F32, ROWS, BKB> {
   }
 };
 
+// E8M0 scales of one k-step (128 k = 4 blocks = one 4-byte word per row) for
+// the BM rows of A and then the BN rows of B: (BM + BN) / 64 dword DMA
+// instructions, one per wave; word r of the stage's scale area belongs to row r.
+template <int BM, int BN, int THREADS>
+struct DmaScale {
+  static_assert((BM + BN) / 64 == THREADS / 64, "one scale load per wave");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff;
+
+  __device__ __forceinline__ void setup(const uint8_t* sa, long long slda, int m0, int mlim,
+                                        const uint8_t* sb, long long sldb, int n0, int N,
+                                        int tid) {
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint8_t* base;
+    if (w * 64 < BM) {
+      const int row = w * 64 + lane;
+      base = sa + (size_t)m0 * slda;
+      voff = (m0 + row < mlim) ? (uint32_t)((size_t)row * slda) : OOB;
+    } else {
+      const int row = w * 64 - BM + lane;
+      base = sb + (size_t)n0 * sldb;
+      voff = (n0 + row < N) ? (uint32_t)((size_t)row * sldb) : OOB;
+    }
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7ffffff0,
+                                           0x00020000);
+  }
+  __device__ __forceinline__ void issue(uint32_t* scales, int k0) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(scales + w * 64), 4, (int)voff, k0 / 32,
+                                             0, 0);
+  }
+};
+
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// MXFP8 fragment of 32 rows for k sub-step s (64 k) of a 128-byte step.  The
+// scaled MFMA takes, per lane of half h = l >> 5, k = 16 h .. 16 h + 15 in
+// bytes 0-15 and k = 32 + 16 h .. in bytes 16-31; block 0 (k < 32) is scaled
+// by the h = 0 lane's scale, block 1 by the h = 1 lane's (lane layout and
+// scale pairing measured on the device).  So the lane reads 16-byte chunks
+// 4 s + h and 4 s + 2 + h of its row.
+template <int ROWS, int BKB>
+struct FragMX {
+  static constexpr int READS = 2;
+  __device__ __forceinline__ static u32x8 load(const u32x4* st, int r0, int s, int lane) {
+    typedef KGeom<BKB> Gm;
+    const int row = r0 + (lane & 31), h = lane >> 5;
+    const u32x4 lo = st[row * Gm::CPR + Gm::slot(row, 4 * s + h)];
+    const u32x4 hi = st[row * Gm::CPR + Gm::slot(row, 4 * s + 2 + h)];
+    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
 // ------------------------------------------------------------------ MFMA step
 
 __device__ __forceinline__ void mma(f32x16& acc, const u32x4& b, const u32x4& a, BF16) {
@@ -333,6 +427,16 @@ __device__ __forceinline__ void mma(f32x16& acc, const u32x4& b, const u32x4& a,
   for (int q = 0; q < 4; ++q)
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(b[q]), __uint_as_float(a[q]), acc,
                                                0, 0, 0);
+}
+
+// Scaled MXFP8 MFMA; the scale words carry the lane's block scale in byte
+// OPSEL (B first, as for bf16).
+template <int OPSEL>
+__device__ __forceinline__ void mma_mx(f32x16& acc, const u32x8& b, const u32x8& a, uint32_t sb,
+                                       uint32_t sa) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, b),
+                                                        __builtin_bit_cast(i32x8, a), acc, 0, 0,
+                                                        OPSEL, (int)sb, OPSEL, (int)sa);
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.  Used where
@@ -505,6 +609,132 @@ __device__ __forceinline__ void epi_srelu_bwd(const S* __restrict__ Hrow, S* __r
   }
 }
 
+// ------------------------------------------------------------------ MXFP8 epilogues
+//
+// An MXFP8 layer's FC1 and dGLU epilogues write their output (A, dH) as two
+// MXFP8 copies quantized from the float32 values: the row copy (blocks of 32
+// along the columns, operand of the next forward or dgrad GEMM) and the
+// expert-segmented column copy (blocks of 32 along the tokens, operand of the
+// weight gradient).  Each 32 x 32 block passes through a wave-private LDS
+// tile (row stride 36 floats, so row reads and column reads are both free of
+// bank conflicts); lanes 0-31 then quantize one row each, lanes 32-63 one
+// column each.
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The lane's 16 values (columns 8 g + 4 h + q of tile row lane & 31).
+__device__ __forceinline__ void mx_stage(float* W, int lane, const float* v) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<f32x4*>(W + r * 36 + 8 * g + 4 * h) =
+        f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+}
+
+// Row r0 + l of the row copy gets columns c0 .. c0 + 31 (rows below rlim);
+// row c0 + l of the column copy gets token positions p0 .. p0 + 31 (when the
+// block starts inside the padded segment, p0 < pend).
+__device__ __forceinline__ void mx_emit(const float* W, int lane, const GemmArgs& p, int r0,
+                                        int rlim, int c0, int p0, int pend) {
+  const int l = lane & 31;
+  float v[32];
+  uint32_t w8[8];
+  if (lane < 32) {
+    const int row = r0 + l;
+    if (p.mxr && row < rlim) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(W + l * 36 + 4 * q);
+        v[4 * q] = t[0];
+        v[4 * q + 1] = t[1];
+        v[4 * q + 2] = t[2];
+        v[4 * q + 3] = t[3];
+      }
+      const uint32_t sc = mx_quant32(v, w8);
+      u32x4* d = reinterpret_cast<u32x4*>(p.mxr + (size_t)row * p.ld_mxr + c0);
+      d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
+      d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+      p.mxr_s[(size_t)row * (p.ld_mxr / 32) + c0 / 32] = (uint8_t)sc;
+    }
+  } else if (p.mxc && p0 < pend) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) v[r] = W[r * 36 + l];
+    const uint32_t sc = mx_quant32(v, w8);
+    u32x4* d = reinterpret_cast<u32x4*>(p.mxc + (size_t)(c0 + l) * p.ld_mxc + p0);
+    d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
+    d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+    p.mxc_s[(size_t)(c0 + l) * (p.ld_mxc / 32) + p0 / 32] = (uint8_t)sc;
+  }
+}
+
+// FC1 + GLU values of one gate/linear block pair: stores H (bf16, nullable
+// row pointer), returns A (zero for rows past the segment).
+template <int ACT>
+__device__ __forceinline__ void glu_fwd_values(uint16_t* __restrict__ Hrow, const f32x16& accg,
+                                               const f32x16& accl, int c0, float L, float alpha,
+                                               int gtanh, bool rok, float* o) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    float gv[4], lv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      gv[q] = accg[4 * g + q];
+      lv[q] = accl[4 * g + q];
+    }
+    if (Hrow) {
+      store4(Hrow + col, gv);
+      store4(Hrow + col + 32, lv);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float gt = gv[q], li = lv[q];
+      if (L > 0.0f) {
+        gt = fminf(gt, L);
+        li = fminf(fmaxf(li, -L), L);
+      }
+      o[4 * g + q] = rok ? act_value<ACT>(gt, alpha, gtanh) * li : 0.0f;
+    }
+  }
+}
+
+// dGLU values of one dA block: gate and linear gradients (zero when Hrow is
+// null, i.e. for rows past the segment).
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_values(const uint16_t* __restrict__ Hrow,
+                                               const f32x16& acc, int c0, float L, float alpha,
+                                               int gtanh, float* dg, float* dl) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    const int pg = (col >> 5) * 64 + (col & 31);
+    float hg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (Hrow) {
+      load4(Hrow + pg, hg);
+      load4(Hrow + pg + 32, hl);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float gt = hg[q], li = hl[q], mg = 1.0f, ml = 1.0f;
+      if (L > 0.0f) {
+        mg = gt <= L ? 1.0f : 0.0f;
+        ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
+        gt = fminf(gt, L);
+        li = fminf(fmaxf(li, -L), L);
+      }
+      float a, da_dg;
+      act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
+      const float d = Hrow ? acc[4 * g + q] : 0.0f;
+      dg[4 * g + q] = d * li * da_dg * mg;
+      dl[4 * g + q] = d * a * ml;
+    }
+  }
+}
+
 // Workgroup barrier for the LDS ring.  __syncthreads() (and any fence whose
 // scope covers LDS) makes the compiler wait for every outstanding load first,
 // including the LDS-DMA loads of later ring stages, which would serialise the
@@ -560,13 +790,20 @@ struct GemmCfg {
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int BKB = TL::BKB;
   static constexpr int BK = BKB / sizeof(typename EL::storage);   // k per pipeline step
-  static constexpr int SUB = BKB / 32;                             // MFMA k sub-steps per step
+  static constexpr bool MX = is_mx<EL>();
+  static constexpr int SUB = MX ? BKB / 64 : BKB / 32;             // MFMA k sub-steps per step
   static constexpr int STAGES = TL::STAGES;                        // LDS ring depth
-  static constexpr int STAGE_U4 = (BM + BN) * (BKB / 16);          // 16-byte units per stage
+  // 16-byte units per stage: the A and B tiles, then (MX) one scale word per row
+  static constexpr int STAGE_U4 = (BM + BN) * (BKB / 16) + (MX ? (BM + BN) / 4 : 0);
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16;
+  // MX epilogues stage 32 x 36 floats per wave in a free ring slot
+  static constexpr int MX_STAGE_FLOATS = 32 * 36;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!epi_glu_fwd(EPI) || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
   static_assert(LDS_BYTES + 8320 <= 160 * 1024, "LDS ring does not fit");
+  static_assert(!MX || (THREADS / 64) * MX_STAGE_FLOATS * 4 <= STAGE_U4 * 16,
+                "MX epilogue staging must fit in one ring slot");
+  static_assert(!MX || BKB == 128, "MX steps are 128 k (four scale blocks, one word)");
 };
 
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL>
@@ -643,6 +880,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
   // ---- tile decode: expert, row / column origin, row limit, k range ----
   struct TileC {
     int e, m0, n0, mlim, kbeg, kend;
+    int kb0;  // first k of the first step (MX weight gradients: kbeg rounded down to a step)
   };
   auto decode = [&](int tile) {
     TileC t;
@@ -687,6 +925,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     t.mlim = __builtin_amdgcn_readfirstlane(t.mlim);
     t.kbeg = __builtin_amdgcn_readfirstlane(t.kbeg);
     t.kend = __builtin_amdgcn_readfirstlane(t.kend);
+    t.kb0 = (C::MX && GROUP == RAGGED_K) ? (t.kbeg & ~(BK - 1)) : t.kbeg;
     return t;
   };
 
@@ -703,24 +942,40 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
   typedef typename std::conditional<BKM, DmaK<EL, BN, THREADS, BKB>,
                                     DmaMN<EL, BN, THREADS, BKB>>::type LoadB;
   constexpr int S_ = C::STAGES;
-  constexpr int PERW = LoadA::PER + LoadB::PER;   // DMA instructions per wave per step
+  constexpr bool MX = C::MX;
+  static_assert(!MX || (AKM && BKM), "MXFP8 operands are K-contiguous");
+  // DMA instructions per wave per step (MX: plus one scale word load)
+  constexpr int PERW = LoadA::PER + LoadB::PER + (MX ? 1 : 0);
+  struct NoScale {};
+  typename std::conditional<MX, DmaScale<BM, BN, THREADS>, NoScale>::type ls;
+  auto scales_of = [&](const u32x4* st) {
+    return reinterpret_cast<uint32_t*>(const_cast<u32x4*>(st) + (BM + BN) * CPR);
+  };
   const S* A = reinterpret_cast<const S*>(p.a);
   LoadA la;
   LoadB lb;
   auto stage_ptr = [&](int st) { return smem + (st % S_) * C::STAGE_U4; };
-  auto nk_of = [&](const TileC& t) { return (t.kend - t.kbeg + BK - 1) / BK; };
+  auto nk_of = [&](const TileC& t) {
+    return t.kend > t.kbeg ? (t.kend - t.kb0 + BK - 1) / BK : 0;
+  };
   // set the loaders up for tile t and issue its first STAGES - 1 steps
   auto prologue = [&](const TileC& t) {
     const S* B = reinterpret_cast<const S*>(p.b);
     if constexpr (GROUP == RAGGED_M) B += (size_t)t.e * p.b_expert_stride;
-    la.setup(A, p.lda, t.m0, t.mlim, t.kend, tid);
-    lb.setup(B, p.ldb, t.n0, p.N, t.kend, tid);
+    la.setup(A, p.lda, t.m0, t.mlim, t.kend, tid, t.kbeg);
+    lb.setup(B, p.ldb, t.n0, p.N, t.kend, tid, t.kbeg);
+    if constexpr (MX) {
+      const uint8_t* SB = p.sb;
+      if constexpr (GROUP == RAGGED_M) SB += (size_t)t.e * p.sb_expert_stride;
+      ls.setup(p.sa, p.slda, t.m0, t.mlim, SB, p.sldb, t.n0, p.N, tid);
+    }
     const int nk = nk_of(t);
 #pragma unroll
     for (int st = 0; st < S_ - 1; ++st)
       if (st < nk) {
-        la.issue(stage_ptr(st), t.kbeg + st * BK);
-        lb.issue(stage_ptr(st) + BM * CPR, t.kbeg + st * BK);
+        la.issue(stage_ptr(st), t.kb0 + st * BK);
+        lb.issue(stage_ptr(st) + BM * CPR, t.kb0 + st * BK);
+        if constexpr (MX) ls.issue(scales_of(stage_ptr(st)), t.kb0 + st * BK);
       }
   };
 
@@ -745,49 +1000,170 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       lds_barrier();
       if (kt + S_ - 1 < nk) {
         u32x4* nb = stage_ptr(kt + S_ - 1);
-        la.issue(nb, cur.kbeg + (kt + S_ - 1) * BK);
-        lb.issue(nb + BM * CPR, cur.kbeg + (kt + S_ - 1) * BK);
+        la.issue(nb, cur.kb0 + (kt + S_ - 1) * BK);
+        lb.issue(nb + BM * CPR, cur.kb0 + (kt + S_ - 1) * BK);
+        if constexpr (MX) ls.issue(scales_of(nb), cur.kb0 + (kt + S_ - 1) * BK);
       }
       const u32x4* As = stage_ptr(kt);
       const u32x4* Bs = As + BM * CPR;
-      // fragments of sub-step s + 1 are read while the MFMAs of s run;
-      // read in order of first use by the i-major MFMA loop: a0, b0 .. b(TN-1), a1 ..
-      u32x4 af[2][TM], bfr[2][TN];
-      auto frags = [&](int buf, int s2) {
-        af[buf][0] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM, s2, lane);
+      if constexpr (MX) {
+        // scale word of each fragment row, shifted so that byte 2 s holds the
+        // block of sub-step s that this lane's half (h) covers: 2 s + h
+        const int h = lane >> 5;
+        const uint32_t* Ss = scales_of(As);
+        uint32_t swa[TM], swb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) swa[i] = Ss[wm * C::WTM + 32 * i + (lane & 31)] >> (8 * h);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bfr[buf][j] = Frag<BKM, EL, BN, BKB>::load(Bs, wn * C::WTN + 32 * j, s2, lane);
+          swb[j] = Ss[BM + wn * C::WTN + 32 * j + (lane & 31)] >> (8 * h);
+        if constexpr (GROUP == RAGGED_K) {
+          // blocks outside the segment read zero codes; their scale bytes
+          // belong to other segments (or were never written): make them 1.0
+          const int b0 = (cur.kb0 + kt * BK) / 32 + h;
+          uint32_t keep = 0xffffffffu, fill = 0u;
 #pragma unroll
-        for (int i = 1; i < TM; ++i)
-          af[buf][i] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM + 32 * i, s2, lane);
-      };
-      frags(0, 0);
+          for (int s2 = 0; s2 < SUB; ++s2) {
+            const int b = b0 + 2 * s2;
+            if (b * 32 < cur.kbeg || b * 32 >= cur.kend) {
+              keep &= ~(0xffu << (16 * s2));
+              fill |= 127u << (16 * s2);
+            }
+          }
 #pragma unroll
-      for (int s2 = 0; s2 < SUB; ++s2) {
-        if (s2 + 1 < SUB) frags((s2 + 1) & 1, s2 + 1);
+          for (int i = 0; i < TM; ++i) swa[i] = (swa[i] & keep) | fill;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+          for (int j = 0; j < TN; ++j) swb[j] = (swb[j] & keep) | fill;
+        }
+        u32x8 af[2][TM], bfr[2][TN];
+        auto frags = [&](int buf, int s2) {
+          af[buf][0] = FragMX<BM, BKB>::load(As, wm * C::WTM, s2, lane);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) mma(acc[i][j], bfr[s2 & 1][j], af[s2 & 1][i], EL());
-      }
-      if constexpr (TL::SCHED == 1) {
-        constexpr int NR = TM * Frag<AKM, EL, BM, BKB>::READS + TN * Frag<BKM, EL, BN, BKB>::READS;
-        constexpr int NM = TM * TN;
-        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-        static_for<0, SUB>([&](auto s2) {
-          static_for<0, NM>([&](auto m) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            constexpr int nr = (NR * (m + 1)) / NM - (NR * m) / NM;
-            if constexpr (s2 + 1 < SUB && nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+          for (int j = 0; j < TN; ++j)
+            bfr[buf][j] = FragMX<BN, BKB>::load(Bs, wn * C::WTN + 32 * j, s2, lane);
+#pragma unroll
+          for (int i = 1; i < TM; ++i)
+            af[buf][i] = FragMX<BM, BKB>::load(As, wm * C::WTM + 32 * i, s2, lane);
+        };
+        frags(0, 0);
+        static_for<0, SUB>([&](auto sc) {
+          constexpr int s2 = decltype(sc)::value;
+          if constexpr (s2 + 1 < SUB) frags((s2 + 1) & 1, s2 + 1);
+          static_for<0, TM>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            static_for<0, TN>([&](auto jc) {
+              constexpr int j = decltype(jc)::value;
+              mma_mx<2 * s2>(acc[i][j], bfr[s2 & 1][j], af[s2 & 1][i], swb[j], swa[i]);
+            });
           });
         });
-      }
+        if constexpr (TL::SCHED == 1) {
+          constexpr int NR = (TM + TN) * FragMX<BM, BKB>::READS;
+          constexpr int NM = TM * TN;
+          __builtin_amdgcn_sched_group_barrier(0x100, NR + TM + TN, 0);
+          static_for<0, SUB>([&](auto s2) {
+            static_for<0, NM>([&](auto m) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              constexpr int nr = (NR * (m + 1)) / NM - (NR * m) / NM;
+              if constexpr (s2 + 1 < SUB && nr > 0)
+                __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+            });
+          });
+        }
+      } else {
+        // fragments of sub-step s + 1 are read while the MFMAs of s run;
+        // read in order of first use by the i-major MFMA loop: a0, b0 .. b(TN-1), a1 ..
+        u32x4 af[2][TM], bfr[2][TN];
+        auto frags = [&](int buf, int s2) {
+          af[buf][0] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM, s2, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bfr[buf][j] = Frag<BKM, EL, BN, BKB>::load(Bs, wn * C::WTN + 32 * j, s2, lane);
+#pragma unroll
+          for (int i = 1; i < TM; ++i)
+            af[buf][i] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM + 32 * i, s2, lane);
+        };
+        frags(0, 0);
+#pragma unroll
+        for (int s2 = 0; s2 < SUB; ++s2) {
+          if (s2 + 1 < SUB) frags((s2 + 1) & 1, s2 + 1);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) mma(acc[i][j], bfr[s2 & 1][j], af[s2 & 1][i], EL());
+        }
+        if constexpr (TL::SCHED == 1) {
+          constexpr int NR = TM * Frag<AKM, EL, BM, BKB>::READS + TN * Frag<BKM, EL, BN, BKB>::READS;
+          constexpr int NM = TM * TN;
+          __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+          static_for<0, SUB>([&](auto s2) {
+            static_for<0, NM>([&](auto m) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              constexpr int nr = (NR * (m + 1)) / NM - (NR * m) / NM;
+              if constexpr (s2 + 1 < SUB && nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+            });
+          });
+        }
+      }  // bf16 / fp32 step
     }
     const int e = cur.e, m0 = cur.m0, n0 = cur.n0, mlim = cur.mlim;
 
     // ---- epilogue: lane holds rows (lane & 31) + 32 i, columns 32 j + 8 g + 4 h + q ----
+    typedef typename OutT<EL>::type SO;
     const int cw = n0 + wn * C::WTN + 4 * (lane >> 5);  // column of the lane's first value
+    if constexpr (MX && (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))) {
+      // every lane takes part (the tile is shared); rows past the segment are
+      // zero in the column copy and skipped in the row copy.  The ring slot
+      // after the last step's is free: its last reader passed the barrier of
+      // the last step, and the next tile's loads start after a barrier.
+      float* Wt = reinterpret_cast<float*>(stage_ptr(nk)) + wave * C::MX_STAGE_FLOATS;
+      const int pe0 = p.pad_offsets ? p.pad_offsets[e] : 0;
+      const int pe1 = p.pad_offsets ? p.pad_offsets[e + 1] : 0;
+      const int off_e = s_off[e];
+      static_for<0, TM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int r0 = m0 + wm * C::WTM + 32 * i;
+        const int row = r0 + (lane & 31);
+        const bool rok = row < mlim;
+        const int prow = pe0 + (r0 - off_e);
+        static_for<0, TN>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const int cb = n0 + wn * C::WTN + 32 * j;
+          if constexpr (epi_glu_fwd(EPI)) {
+            if constexpr ((j & 1) == 0) {
+              if (cb < p.N) {
+                float o[16];
+                glu_fwd_values<epi_act(EPI)>(
+                    (rok && p.aux) ? reinterpret_cast<SO*>(p.aux) + (size_t)row * p.ld_aux
+                                   : nullptr,
+                    acc[i][j], acc[i][j + 1], cb + 4 * (lane >> 5), p.clamp, p.alpha,
+                    p.gelu_tanh, rok, o);
+                mx_stage(Wt, lane, o);
+                wave_lds_sync();
+                mx_emit(Wt, lane, p, r0, mlim, (cb >> 6) * 32, prow, pe1);
+                wave_lds_sync();
+              }
+            }
+          } else {
+            if (cb < p.N) {
+              float dg[16], dl[16];
+              glu_bwd_values<epi_act(EPI)>(
+                  rok ? reinterpret_cast<const SO*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
+                  acc[i][j], cb + 4 * (lane >> 5), p.clamp, p.alpha, p.gelu_tanh, dg, dl);
+              const int pg0 = (cb >> 5) * 64;
+              mx_stage(Wt, lane, dg);
+              wave_lds_sync();
+              mx_emit(Wt, lane, p, r0, mlim, pg0, prow, pe1);
+              wave_lds_sync();
+              mx_stage(Wt, lane, dl);
+              wave_lds_sync();
+              mx_emit(Wt, lane, p, r0, mlim, pg0 + 32, prow, pe1);
+              wave_lds_sync();
+            }
+          }
+        });
+      });
+    } else
     static_for<0, TM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int row = m0 + wm * C::WTM + 32 * i + (lane & 31);
@@ -796,7 +1172,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
           constexpr int j = decltype(jc)::value;
           const int c0 = cw + 32 * j;
           if constexpr (EPI == EPI_STORE && GROUP == RAGGED_M) {
-            epi_store<S>(reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc,
+            epi_store<SO>(reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc,
                          p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], c0, p.N);
           } else if constexpr (EPI == EPI_STORE) {
             epi_store_f32(reinterpret_cast<float*>(p.c) + (size_t)e * p.c_expert_stride +
@@ -804,24 +1180,24 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                           acc[i][j], c0, p.N, p.accumulate);
           } else if constexpr (epi_glu_fwd(EPI)) {
             if constexpr ((j & 1) == 0)
-              epi_glu_fwd<epi_act(EPI), S>(
-                  p.aux ? reinterpret_cast<S*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
-                  reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc,
+              epi_glu_fwd<epi_act(EPI), SO>(
+                  p.aux ? reinterpret_cast<SO*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
+                  reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc,
                   p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], acc[i][j + 1],
                   c0, p.N, p.clamp, p.alpha, p.gelu_tanh);
           } else if constexpr (epi_glu_bwd(EPI)) {
-            epi_glu_bwd<epi_act(EPI), S>(
-                reinterpret_cast<const S*>(p.aux) + (size_t)row * p.ld_aux,
-                reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0, p.N, p.clamp,
+            epi_glu_bwd<epi_act(EPI), SO>(
+                reinterpret_cast<const SO*>(p.aux) + (size_t)row * p.ld_aux,
+                reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0, p.N, p.clamp,
                 p.alpha, p.gelu_tanh);
           } else if constexpr (EPI == EPI_SRELU_FWD) {
-            epi_srelu_fwd<S>(
-                p.aux ? reinterpret_cast<S*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
-                reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc,
+            epi_srelu_fwd<SO>(
+                p.aux ? reinterpret_cast<SO*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
+                reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc,
                 p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], c0, p.N, p.clamp);
           } else if constexpr (EPI == EPI_SRELU_BWD) {
-            epi_srelu_bwd<S>(reinterpret_cast<const S*>(p.aux) + (size_t)row * p.ld_aux,
-                             reinterpret_cast<S*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0,
+            epi_srelu_bwd<SO>(reinterpret_cast<const SO*>(p.aux) + (size_t)row * p.ld_aux,
+                             reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0,
                              p.N, p.clamp);
           }
         });
@@ -899,6 +1275,17 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
   }
 }
 
+// MXFP8 operands: 8 waves at 256 x 256 (one scale-word load per wave), or
+// 4 waves at 128 x 128 for small problems.
+typedef Tile<256, 256, 2, 4, 128, 2, 1> TMxBig;
+typedef Tile<128, 128, 2, 2, 128, 2> TMxSmall;
+
+template <int GROUP, int EPI>
+moe_status_t dispatch_mx(const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
+  if (big) return launch_gemm<MX8, true, true, GROUP, EPI, TMxBig>(p, max_cus, s);
+  return launch_gemm<MX8, true, true, GROUP, EPI, TMxSmall>(p, max_cus, s);
+}
+
 template <bool AKM, bool BKM, int GROUP, int EPI>
 moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
   if (dtype == MOE_BF16) return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
@@ -929,13 +1316,172 @@ inline bool big_ragged_k(int R, int E, int M, int N) {
 
 using namespace moe;
 
+// An MXFP8 GEMM operand with reduction length K: ld a multiple of 128 (whole
+// scale words per k-step) and at least K.
+inline bool mx_in_ok(const moe_mx_t* m, long long K) {
+  return m && m->data && m->scale && m->ld >= K && m->ld % 128 == 0 && aligned16(m->data) &&
+         aligned16(m->scale);
+}
+inline bool mx_out_ok(const moe_mx_t* m, long long n) {
+  return m && m->data && m->scale && m->ld >= n && m->ld % 32 == 0 && aligned16(m->data);
+}
+inline void set_mx_a(GemmArgs& p, const moe_mx_t* m) {
+  p.a = m->data;
+  p.lda = m->ld;
+  p.sa = m->scale;
+  p.slda = m->ld / 32;
+}
+inline void set_mx_b(GemmArgs& p, const moe_mx_t* m, long long rows_per_expert) {
+  p.b = m->data;
+  p.ldb = m->ld;
+  p.sb = m->scale;
+  p.sldb = m->ld / 32;
+  p.b_expert_stride = rows_per_expert * m->ld;
+  p.sb_expert_stride = rows_per_expert * (m->ld / 32);
+}
+inline void set_mx_out(GemmArgs& p, moe_mx_t* row, moe_mx_t* col, const int32_t* pad) {
+  if (row) {
+    p.mxr = row->data;
+    p.mxr_s = row->scale;
+    p.ld_mxr = row->ld;
+  }
+  if (col) {
+    p.mxc = col->data;
+    p.mxc_s = col->scale;
+    p.ld_mxc = col->ld;
+  }
+  p.pad_offsets = pad;
+}
+
+// MXFP8 FC1 + GLU (dtype == MOE_E4M3).
+moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
+  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_glu_fwd_args_t));
+  MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU);
+  MOE_CHECK_ARG(a->b1p == nullptr && a->d % 128 == 0);
+  if (a->R == 0) return MOE_OK;
+  const int n1 = 2 * a->f;
+  MOE_CHECK_ARG(a->offsets && mx_in_ok(a->xp_mx, a->d) && mx_in_ok(a->w1_mx, a->d));
+  MOE_CHECK_ARG(!a->a_row || mx_out_ok(a->a_row, a->f));
+  MOE_CHECK_ARG(!a->a_col || (mx_out_ok(a->a_col, moe_mx_col_len(a->R, a->E)) && a->pad_offsets));
+  MOE_CHECK_ARG(aligned16(a->h_out));
+  GemmArgs p = zero_args();
+  set_mx_a(p, a->xp_mx);
+  set_mx_b(p, a->w1_mx, n1);
+  p.offsets = a->offsets;
+  p.E = a->E;
+  p.R = a->R;
+  p.N = n1;
+  p.K = a->d;
+  p.aux = a->h_out;
+  p.ld_aux = n1;
+  set_mx_out(p, a->a_row, a->a_col, a->pad_offsets);
+  p.clamp = a->clamp;
+  p.alpha = a->alpha;
+  p.act = a->act;
+  p.gelu_tanh = a->gelu_tanh;
+  const bool big = big_ragged_m(a->R, a->E, n1);
+  if (a->act == MOE_ACT_SWIGLU) return dispatch_mx<RAGGED_M, EPI_SWIGLU_FWD>(p, big, a->max_cus, s);
+  return dispatch_mx<RAGGED_M, EPI_GEGLU_FWD>(p, big, a->max_cus, s);
+}
+
+moe_status_t gemm_fwd_mx(const moe_gemm_fwd_args_t* a, hipStream_t s) {
+  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_gemm_fwd_args_t));
+  MOE_CHECK_ARG(a->b == nullptr && a->K % 128 == 0);
+  if (a->R == 0) return MOE_OK;
+  MOE_CHECK_ARG(a->offsets && a->y && aligned16(a->y));
+  MOE_CHECK_ARG(mx_in_ok(a->a_mx, a->K) && mx_in_ok(a->w_mx, a->K));
+  GemmArgs p = zero_args();
+  set_mx_a(p, a->a_mx);
+  set_mx_b(p, a->w_mx, a->N);
+  p.offsets = a->offsets;
+  p.E = a->E;
+  p.R = a->R;
+  p.N = a->N;
+  p.K = a->K;
+  p.c = a->y;
+  p.ldc = a->N;
+  return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->N), a->max_cus, s);
+}
+
+moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
+  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_glu_bwd_args_t));
+  MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU);
+  MOE_CHECK_ARG(a->d % 128 == 0);
+  if (a->R == 0) return MOE_OK;
+  const int n1 = 2 * a->f;
+  MOE_CHECK_ARG(a->offsets && a->h && aligned16(a->h));
+  MOE_CHECK_ARG(mx_in_ok(a->dy_mx, a->d) && mx_in_ok(a->w2t_mx, a->d));
+  MOE_CHECK_ARG(!a->dh_row || mx_out_ok(a->dh_row, n1));
+  MOE_CHECK_ARG(!a->dh_col ||
+                (mx_out_ok(a->dh_col, moe_mx_col_len(a->R, a->E)) && a->pad_offsets));
+  GemmArgs p = zero_args();
+  set_mx_a(p, a->dy_mx);
+  set_mx_b(p, a->w2t_mx, a->f);
+  p.offsets = a->offsets;
+  p.E = a->E;
+  p.R = a->R;
+  p.N = a->f;
+  p.K = a->d;
+  p.aux = const_cast<void*>(a->h);
+  p.ld_aux = n1;
+  set_mx_out(p, a->dh_row, a->dh_col, a->pad_offsets);
+  p.clamp = a->clamp;
+  p.alpha = a->alpha;
+  p.act = a->act;
+  p.gelu_tanh = a->gelu_tanh;
+  const bool big = big_ragged_m(a->R, a->E, a->f);
+  if (a->act == MOE_ACT_SWIGLU) return dispatch_mx<RAGGED_M, EPI_SWIGLU_BWD>(p, big, a->max_cus, s);
+  return dispatch_mx<RAGGED_M, EPI_GEGLU_BWD>(p, big, a->max_cus, s);
+}
+
+moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
+  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_gemm_bwd_args_t));
+  GemmArgs p = zero_args();
+  p.E = a->E;
+  if (a->mode == MOE_BWD_DGRAD) {
+    // da [R, K] = g [R, N] @ w[e] [N, K] with w given transposed, [K, N] per expert
+    MOE_CHECK_ARG(a->N % 128 == 0);
+    if (a->R == 0) return MOE_OK;
+    MOE_CHECK_ARG(a->offsets && mx_in_ok(a->g_mx, a->N) && mx_in_ok(a->w_mx, a->N));
+    set_mx_a(p, a->g_mx);
+    set_mx_b(p, a->w_mx, a->K);
+    p.offsets = a->offsets;
+    p.R = a->R;
+    p.N = a->K;
+    p.K = a->N;
+    p.c = a->out;
+    p.ldc = a->K;
+    return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->K), a->max_cus, s);
+  }
+  // dw[e] [N, K] = g_col[:, seg e] @ a_col[:, seg e]^T; the k ranges are the
+  // padded segments, so the offsets table is pad_offsets and R its bound
+  MOE_CHECK_ARG(a->db == nullptr && a->pad_offsets);
+  const long long L = moe_mx_col_len(a->R, a->E);
+  MOE_CHECK_ARG(mx_in_ok(a->g_mx, L) && mx_in_ok(a->a_mx, L));
+  MOE_CHECK_ARG(L <= 0x7fffffff);
+  set_mx_a(p, a->g_mx);
+  set_mx_b(p, a->a_mx, 0);
+  p.offsets = a->pad_offsets;
+  p.R = (int)L;
+  p.M = a->N;
+  p.N = a->K;
+  p.c = a->out;
+  p.ldc = a->K;
+  p.c_expert_stride = (long long)a->N * a->K;
+  p.accumulate = a->accumulate;
+  return dispatch_mx<RAGGED_K, EPI_STORE>(p, big_ragged_k(a->R, a->E, a->N, a->K), a->max_cus,
+                                          s);
+}
+
 extern "C" {
 
 moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream) {
-  MOE_CHECK_ARG(a && a->struct_size >= sizeof(moe_glu_fwd_args_t));
-  MOE_CHECK_ARG(valid_dtype(a->dtype) && a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
+  MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_glu_fwd_args_t, xp_mx));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->d > 0 && a->f > 0 && a->d % 32 == 0 && a->f % 32 == 0);
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU || a->act == MOE_ACT_SRELU);
+  if (a->dtype == MOE_E4M3) return glu_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->xp && a->w1p && a->offsets && a->a_out);
   MOE_CHECK_ARG(aligned16(a->xp) && aligned16(a->w1p) && aligned16(a->a_out) &&
@@ -973,9 +1519,11 @@ moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream)
 }
 
 moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* a, void* stream) {
-  MOE_CHECK_ARG(a && a->struct_size >= sizeof(moe_gemm_fwd_args_t));
-  MOE_CHECK_ARG(valid_dtype(a->dtype) && a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
+  MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_gemm_fwd_args_t, a_mx));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->N > 0 && a->K > 0 && a->N % 8 == 0 && a->K % 8 == 0);
+  if (a->dtype == MOE_E4M3) return gemm_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->a && a->w && a->offsets && a->y);
   MOE_CHECK_ARG(aligned16(a->a) && aligned16(a->w) && aligned16(a->y) && aligned16(a->b));
@@ -1000,10 +1548,12 @@ moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* a, void* stream) {
 }
 
 moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream) {
-  MOE_CHECK_ARG(a && a->struct_size >= sizeof(moe_glu_bwd_args_t));
-  MOE_CHECK_ARG(valid_dtype(a->dtype) && a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
+  MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_glu_bwd_args_t, dy_mx));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->d > 0 && a->f > 0 && a->d % 32 == 0 && a->f % 32 == 0);
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU || a->act == MOE_ACT_SRELU);
+  if (a->dtype == MOE_E4M3) return glu_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->dy && a->w2 && a->h && a->offsets && a->dh);
   MOE_CHECK_ARG(aligned16(a->dy) && aligned16(a->w2) && aligned16(a->h) && aligned16(a->dh));
@@ -1038,11 +1588,14 @@ moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream)
 }
 
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
-  MOE_CHECK_ARG(a && a->struct_size >= sizeof(moe_gemm_bwd_args_t));
-  MOE_CHECK_ARG(valid_dtype(a->dtype) && a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
+  MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_gemm_bwd_args_t, g_mx));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->N > 0 && a->K > 0 && a->N % 8 == 0 && a->K % 8 == 0);
   MOE_CHECK_ARG(a->mode == MOE_BWD_DGRAD || a->mode == MOE_BWD_WGRAD);
-  MOE_CHECK_ARG(a->g && a->offsets && a->out && aligned16(a->g) && aligned16(a->out));
+  MOE_CHECK_ARG(a->out && aligned16(a->out));
+  if (a->dtype == MOE_E4M3) return gemm_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  MOE_CHECK_ARG(a->g && a->offsets && aligned16(a->g));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   GemmArgs p = zero_args();
   p.offsets = a->offsets;

@@ -10,6 +10,13 @@ Forward:  route top-k -> permute -> FC1 + GLU epilogue -> FC2 -> combine.
 Backward: combine bwd (dY, dgate) -> route bwd (dlogits) -> FC2 dgrad + dGLU
 (dH) -> FC2 wgrad (dW2, db2) -> FC1 dgrad (dXp) -> FC1 wgrad (dW1p, db1p) ->
 unpermute-sum (dX).
+
+MXFP8 variant (``gemm="mxfp8"``): every GEMM operand is an MXFP8 copy blocked
+along that GEMM's reduction axis.  Xp and dY exist only as MXFP8 row and
+expert-segmented column copies written straight from x and d_out; FC1's
+epilogue writes A, and the dGLU epilogue dH, as the same two copies; H stays
+bf16 for the dGLU.  Weights are quantized once (``mx_weights``) into row and
+transposed copies.
 """
 from __future__ import annotations
 
@@ -20,11 +27,27 @@ import torch
 from . import ops
 
 
+class MXWeights:
+    """MXFP8 copies of the expert weights: W1p [E, 2f, d] blocked along d (FC1)
+    and along 2f (FC1 dgrad, stored transposed [E*d, 2f]); W2 [E, d, f] along f
+    (FC2) and along d (FC2 dgrad, stored transposed [E*f, d])."""
+
+    def __init__(self, W1p, W2):
+        E, n1, d = W1p.shape
+        self.w1 = ops.moe_mx_quantize(W1p.reshape(E * n1, d))
+        self.w1t = ops.moe_mx_quantize_transpose(W1p)
+        self.w2 = ops.moe_mx_quantize(W2.reshape(-1, W2.shape[2]))
+        self.w2t = ops.moe_mx_quantize_transpose(W2)
+
+
 class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
-                 backward=True, device="cuda", max_cus=0):
+                 backward=True, device="cuda", max_cus=0, gemm="bf16"):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
+        self.mx = gemm == "mxfp8"
+        if self.mx and (bias or act == "srelu" or dtype != torch.bfloat16):
+            raise ValueError("the MXFP8 variant is gated, bias-free, with bf16 activations")
         self.R = R = T * k
         self.dtype, self.act, self.score, self.normalize = dtype, act, score, normalize
         self.clamp, self.alpha, self.gelu_tanh = clamp, alpha, gelu_tanh
@@ -44,13 +67,16 @@ class MoEFFN:
         self.row_map = z((T, k), i32)
         self.src_row = z((R,), i32)
         self.ws = z((ops.moe_permute_workspace_size(T, E, k),), torch.uint8)
+        self.has_backward = backward
+        self.timer = None          # optional OpTimer: HIP events around each library call
+        if self.mx:
+            self._alloc_mx(z, dev)
+            return
         self.xp = z((R, d), dtype)
         self.H = z((R, n1), dtype) if backward else None
         self.A = z((R, f), dtype)
         self.Y = z((R, d), dtype)
         self.out = z((T, d), dtype)
-        self.has_backward = backward
-        self.timer = None          # optional OpTimer: HIP events around each library call
         if backward:
             self.dY = z((R, d), dtype)
             self.dgate = z((T, k), f32)
@@ -63,12 +89,43 @@ class MoEFFN:
             self.db1p = z((E, n1), f32) if bias else None
             self.db2 = z((E, d), f32) if bias else None
 
+    def _alloc_mx(self, z, dev):
+        T, d, f, E, R, n1 = self.T, self.d, self.f, self.E, self.R, self.n1
+        L = ops.moe_mx_col_len(R, E)
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+
+        def mx(rows, ld):
+            return ops.MXTensor(rows, ld, dev, z((rows, ld), u8), z((rows, ld // 32), u8))
+
+        self.pad_offsets = z((E + 1,), torch.int32)
+        self.xp_row, self.xp_col = mx(R, d), mx(d, L)
+        self.H = z((R, n1), bf)
+        self.A_row, self.A_col = mx(R, f), mx(f, L)
+        self.Y = z((R, d), bf)
+        self.out = z((T, d), bf)
+        if self.has_backward:
+            self.dgate = z((T, self.k), f32)
+            self.dlogits = z((T, E), f32)
+            self.dY_row, self.dY_col = mx(R, d), mx(d, L)
+            self.dH_row, self.dH_col = mx(R, n1), mx(n1, L)
+            self.dXp = z((R, d), bf)
+            self.dX = z((T, d), bf)
+            self.dW1p = z((E, n1, d), f32)
+            self.dW2 = z((E, d, f), f32)
+            self.db1p = self.db2 = None
+
+    @staticmethod
+    def mx_weights(W1p, W2):
+        return MXWeights(W1p, W2)
+
     # ------------------------------------------------------------------ passes
 
     def _op(self, name):
         return self.timer.op(name) if self.timer is not None else contextlib.nullcontext()
 
     def forward(self, x, logits, W1p, W2, b1p=None, b2=None):
+        if self.mx:
+            return self._forward_mx(x, logits, W1p)
         with self._op("route_topk"):
             ops.moe_route_topk(logits, self.k, self.score, self.normalize, self.topk_idx,
                                self.topk_w, self.err)
@@ -91,6 +148,8 @@ class MoEFFN:
     def backward(self, d_out, logits, W1p, W2):
         if not self.has_backward:
             raise RuntimeError("layer built without backward buffers")
+        if self.mx:
+            return self._backward_mx(d_out, logits, W1p)
         with self._op("combine_bwd"):
             ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w, d_y=self.dY,
                                           d_topk_w=self.dgate)
@@ -111,6 +170,67 @@ class MoEFFN:
         with self._op("fc1_wgrad"):
             ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="wgrad", a=self.xp,
                                      out=self.dW1p, db=self.db1p, max_cus=self.max_cus)
+        with self._op("unpermute_dx"):
+            ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
+        return self.dX
+
+    def _forward_mx(self, x, logits, W: MXWeights):
+        E, R, f, d = self.E, self.R, self.f, self.d
+        with self._op("route_topk"):
+            ops.moe_route_topk(logits, self.k, self.score, self.normalize, self.topk_idx,
+                               self.topk_w, self.err)
+        with self._op("permute"):
+            ops.moe_permute(x, self.topk_idx, E, counts=self.counts, offsets=self.offsets,
+                            pad_offsets=self.pad_offsets, row_map=self.row_map,
+                            src_row=self.src_row, ws=self.ws, err_word=self.err, gather=False)
+        with self._op("quantize_x"):
+            ops.moe_mx_quantize_experts(x, self.offsets, self.pad_offsets, R, src_row=self.src_row,
+                                        row_out=self.xp_row, col_out=self.xp_col,
+                                        want_col=self.has_backward)
+        with self._op("fc1_glu_fwd"):
+            ops.moe_grouped_gemm_glu_fwd(self.xp_row, W.w1, self.offsets, E=E, f=f, act=self.act,
+                                         clamp=self.clamp, alpha=self.alpha,
+                                         gelu_tanh=self.gelu_tanh, h_out=self.H,
+                                         pad_offsets=self.pad_offsets, a_row=self.A_row,
+                                         a_col=self.A_col, want_col=self.has_backward,
+                                         max_cus=self.max_cus)
+        with self._op("fc2_fwd"):
+            ops.moe_grouped_gemm_fwd(self.A_row, W.w2, self.offsets, E=E, N=d, y=self.Y,
+                                     max_cus=self.max_cus)
+        with self._op("combine"):
+            ops.moe_unpermute_combine(self.Y, self.row_map, self.topk_w, out=self.out)
+        return self.out
+
+    def _backward_mx(self, d_out, logits, W: MXWeights):
+        E, R, d = self.E, self.R, self.d
+        with self._op("combine_bwd"):
+            ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w,
+                                          d_topk_w=self.dgate, want_dy=False)
+        with self._op("route_topk_bwd"):
+            ops.moe_route_topk_bwd(logits, self.topk_idx, self.dgate, self.score,
+                                   self.normalize, d_logits=self.dlogits)
+        with self._op("quantize_dy"):
+            ops.moe_mx_quantize_experts(d_out, self.offsets, self.pad_offsets, R,
+                                        src_row=self.src_row, row_map=self.row_map,
+                                        topk_w=self.topk_w, row_out=self.dY_row,
+                                        col_out=self.dY_col)
+        with self._op("fc2_dgrad_dglu"):
+            ops.moe_grouped_gemm_glu_bwd(self.dY_row, W.w2t, self.H, self.offsets, E=E,
+                                         act=self.act, clamp=self.clamp, alpha=self.alpha,
+                                         gelu_tanh=self.gelu_tanh, pad_offsets=self.pad_offsets,
+                                         dh_row=self.dH_row, dh_col=self.dH_col,
+                                         max_cus=self.max_cus)
+        with self._op("fc2_wgrad"):
+            ops.moe_grouped_gemm_bwd(self.dY_col, self.offsets, mode="wgrad", a=self.A_col,
+                                     out=self.dW2, E=E, R=R, pad_offsets=self.pad_offsets,
+                                     max_cus=self.max_cus)
+        with self._op("fc1_dgrad"):
+            ops.moe_grouped_gemm_bwd(self.dH_row, self.offsets, mode="dgrad", w=W.w1t,
+                                     out=self.dXp, E=E, K=d, max_cus=self.max_cus)
+        with self._op("fc1_wgrad"):
+            ops.moe_grouped_gemm_bwd(self.dH_col, self.offsets, mode="wgrad", a=self.xp_col,
+                                     out=self.dW1p, E=E, R=R, pad_offsets=self.pad_offsets,
+                                     max_cus=self.max_cus)
         with self._op("unpermute_dx"):
             ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
         return self.dX

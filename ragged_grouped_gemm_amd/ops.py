@@ -42,6 +42,73 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+class MXTensor:
+    """An MXFP8 matrix (moe_mx_t): E4M3 codes ``data`` [rows, ld] (uint8) and
+    E8M0 scales ``scale`` [rows, ld / 32] (uint8)."""
+
+    def __init__(self, rows: int, ld: int, device, data=None, scale=None):
+        if ld % 32:
+            raise ValueError("ld must be a multiple of 32")
+        self.ld = ld
+        self.data = torch.empty((rows, ld), dtype=torch.uint8, device=device) if data is None else data
+        self.scale = (torch.empty((rows, ld // 32), dtype=torch.uint8, device=device)
+                      if scale is None else scale)
+
+    @property
+    def rows(self):
+        return self.data.shape[0]
+
+    def c(self):
+        """The ctypes moe_mx_t (keep it referenced while the call runs)."""
+        return _lib.MxT(_p(self.data), _p(self.scale), self.ld)
+
+
+def _mx(m: Optional[MXTensor]):
+    return None if m is None else ctypes.pointer(m.c())
+
+
+def moe_mx_col_len(R: int, E: int) -> int:
+    return int(_lib.load().moe_mx_col_len(R, E))
+
+
+def moe_mx_quantize(x, out: Optional[MXTensor] = None) -> MXTensor:
+    """Row copy of x [rows, n] (blocks of 32 along n)."""
+    x2 = x.reshape(-1, x.shape[-1])
+    rows, n = x2.shape
+    out = MXTensor(rows, n, x.device) if out is None else out
+    check(_lib.load().moe_mx_quantize(_p(x2), _dtype(x), rows, n, _mx(out), _stream()),
+          "moe_mx_quantize")
+    return out
+
+
+def moe_mx_quantize_transpose(x, out: Optional[MXTensor] = None) -> MXTensor:
+    """Transposed copy of x [B, rows, n]: row b*n + c = column c of x[b], blocked along rows."""
+    B, rows, n = x.shape
+    out = MXTensor(B * n, rows, x.device) if out is None else out
+    check(_lib.load().moe_mx_quantize_transpose(_p(x), _dtype(x), B, rows, n, _mx(out),
+                                                _stream()),
+          "moe_mx_quantize_transpose")
+    return out
+
+
+def moe_mx_quantize_experts(x, offsets, pad_offsets, R, *, src_row=None, row_map=None,
+                            topk_w=None, want_row=True, want_col=True, row_out=None,
+                            col_out=None):
+    """Row and/or expert-segmented column copies of v[r] = x[src_row[r]] (* gate)."""
+    n = x.shape[1]
+    E = offsets.shape[0] - 1
+    k = row_map.shape[1] if row_map is not None else 0
+    if want_row and row_out is None:
+        row_out = MXTensor(R, n, x.device)
+    if want_col and col_out is None:
+        col_out = MXTensor(n, moe_mx_col_len(R, E), x.device)
+    check(_lib.load().moe_mx_quantize_experts(
+        _p(x), _dtype(x), _p(src_row), _p(row_map), _p(topk_w), k, _p(offsets),
+        _p(pad_offsets), E, R, n, _mx(row_out if want_row else None),
+        _mx(col_out if want_col else None), _stream()), "moe_mx_quantize_experts")
+    return (row_out if want_row else None), (col_out if want_col else None)
+
+
 def moe_version() -> str:
     return _lib.load().moe_version().decode()
 
@@ -121,8 +188,32 @@ def moe_repack_glu_weights(w, b=None, inverse=False, w_out=None, b_out=None):
 
 
 def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=0.0, alpha=1.0,
-                             gelu_tanh=False, save_h=True, h_out=None, a_out=None, max_cus=0):
-    """FC1 + GLU epilogue.  Returns (A [R, f], H [R, n1] or None)."""
+                             gelu_tanh=False, save_h=True, h_out=None, a_out=None, max_cus=0,
+                             E=None, f=None, pad_offsets=None, a_row=None, a_col=None,
+                             want_row=True, want_col=True):
+    """FC1 + GLU epilogue.  Returns (A [R, f], H [R, n1] or None).
+
+    MXFP8 operands (xp, w1p MXTensor row copies along d; E and f given):
+    returns ((A row copy, A column copy), H bf16)."""
+    if isinstance(xp, MXTensor):
+        R, d = xp.rows, xp.ld
+        n1 = 2 * f
+        dev = xp.data.device
+        if want_row and a_row is None:
+            a_row = MXTensor(R, f, dev)
+        if want_col and a_col is None:
+            a_col = MXTensor(f, moe_mx_col_len(R, E), dev)
+        if save_h and h_out is None:
+            h_out = torch.empty((R, n1), dtype=torch.bfloat16, device=dev)
+        args = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _lib.MOE_E4M3, None, None, None,
+                               _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
+                               _p(h_out) if save_h else None, None, max_cus, _mx(xp), _mx(w1p),
+                               _mx(a_row if want_row else None),
+                               _mx(a_col if want_col else None), _p(pad_offsets))
+        check(_lib.load().moe_grouped_gemm_glu_fwd(ctypes.byref(args), _stream()),
+              "moe_grouped_gemm_glu_fwd")
+        return ((a_row if want_row else None), (a_col if want_col else None)), \
+            (h_out if save_h else None)
     R, d = xp.shape
     E, n1, _ = w1p.shape
     f = n1 if act == "srelu" else n1 // 2
@@ -137,8 +228,17 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
     return a_out, (h_out if save_h else None)
 
 
-def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0):
-    """y[r] = a[r] @ w[e]^T (+ b[e])."""
+def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0, E=None, N=None):
+    """y[r] = a[r] @ w[e]^T (+ b[e]).  MXFP8 operands (a, w MXTensor row copies
+    along K; E and N given): y is bf16."""
+    if isinstance(a, MXTensor):
+        R, K = a.rows, a.ld
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=a.data.device) if y is None else y
+        args = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), _lib.MOE_E4M3, None, None, None,
+                                _p(offsets), E, R, N, K, _p(y), max_cus, _mx(a), _mx(w))
+        check(_lib.load().moe_grouped_gemm_fwd(ctypes.byref(args), _stream()),
+              "moe_grouped_gemm_fwd")
+        return y
     R, K = a.shape
     E, N, _ = w.shape
     y = _empty((R, N), a.dtype, a) if y is None else y
@@ -149,8 +249,28 @@ def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0):
 
 
 def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alpha=1.0,
-                             gelu_tanh=False, dh=None, max_cus=0):
-    """FC2 dgrad + dGLU epilogue -> dH [R, n1] (packed like h)."""
+                             gelu_tanh=False, dh=None, max_cus=0, E=None, pad_offsets=None,
+                             dh_row=None, dh_col=None, want_row=True, want_col=True):
+    """FC2 dgrad + dGLU epilogue -> dH [R, n1] (packed like h).
+
+    MXFP8 operands (dy row copy along d, w2 the transposed copy [E*f, d]; E
+    given; h bf16): returns (dH row copy, dH column copy)."""
+    if isinstance(dy, MXTensor):
+        R, d = dy.rows, dy.ld
+        n1 = h.shape[1]
+        f = n1 // 2
+        dev = h.device
+        if want_row and dh_row is None:
+            dh_row = MXTensor(R, n1, dev)
+        if want_col and dh_col is None:
+            dh_col = MXTensor(n1, moe_mx_col_len(R, E), dev)
+        args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), _lib.MOE_E4M3, None, None, _p(h),
+                               _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
+                               None, max_cus, _mx(dy), _mx(w2), _mx(dh_row if want_row else None),
+                               _mx(dh_col if want_col else None), _p(pad_offsets))
+        check(_lib.load().moe_grouped_gemm_glu_bwd(ctypes.byref(args), _stream()),
+              "moe_grouped_gemm_glu_bwd")
+        return (dh_row if want_row else None), (dh_col if want_col else None)
     R, d = dy.shape
     E, _, f = w2.shape
     dh = torch.empty_like(h) if dh is None else dh
@@ -163,8 +283,34 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
 
 
 def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None, want_db=False,
-                         accumulate=False, max_cus=0):
-    """mode "dgrad": da = g @ w[e];  mode "wgrad": dw[e] = g[seg]^T @ a[seg] (+ db)."""
+                         accumulate=False, max_cus=0, E=None, R=None, N=None, K=None,
+                         pad_offsets=None):
+    """mode "dgrad": da = g @ w[e];  mode "wgrad": dw[e] = g[seg]^T @ a[seg] (+ db).
+
+    MXFP8 operands: dgrad takes g [R, N] row copy and w transposed [E*K, N]
+    (E, K given; da bf16); wgrad takes g [N, L] and a [K, L] column copies
+    (E, R given, pad_offsets)."""
+    if isinstance(g, MXTensor):
+        dev = g.data.device
+        if mode == "dgrad":
+            R, N = g.rows, g.ld
+            out = torch.empty((R, K), dtype=torch.bfloat16, device=dev) if out is None else out
+            m = _lib.MOE_BWD_DGRAD
+            args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_E4M3, m, None, None,
+                                    None, _p(offsets), E, R, N, K, _p(out), None, 0, max_cus,
+                                    _mx(g), None, _mx(w), None)
+        elif mode == "wgrad":
+            N, K = g.rows, a.rows
+            out = torch.empty((E, N, K), dtype=torch.float32, device=dev) if out is None else out
+            m = _lib.MOE_BWD_WGRAD
+            args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_E4M3, m, None, None,
+                                    None, _p(offsets), E, R, N, K, _p(out), None, int(accumulate),
+                                    max_cus, _mx(g), _mx(a), None, _p(pad_offsets))
+        else:
+            raise ValueError(mode)
+        check(_lib.load().moe_grouped_gemm_bwd(ctypes.byref(args), _stream()),
+              "moe_grouped_gemm_bwd")
+        return out
     R, N = g.shape
     if mode == "dgrad":
         E, _, K = w.shape
@@ -196,10 +342,11 @@ def moe_unpermute_combine(y, row_map, topk_w=None, out=None):
     return out
 
 
-def moe_unpermute_combine_bwd(d_out, y, row_map, topk_w, d_y=None, d_topk_w=None):
+def moe_unpermute_combine_bwd(d_out, y, row_map, topk_w, d_y=None, d_topk_w=None, want_dy=True):
     T, k = row_map.shape
     d = y.shape[1]
-    d_y = torch.empty_like(y) if d_y is None else d_y
+    if want_dy and d_y is None:
+        d_y = torch.empty_like(y)
     d_topk_w = _empty((T, k), torch.float32, y) if d_topk_w is None else d_topk_w
     check(_lib.load().moe_unpermute_combine_bwd(_p(d_out), _p(y), _dtype(y), _p(row_map),
                                                 _p(topk_w), T, k, d, _p(d_y), _p(d_topk_w),

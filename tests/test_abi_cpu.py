@@ -64,6 +64,46 @@ def test_bad_arguments_rejected(lib):
     assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
 
 
+def test_mx_host_checks():
+    """MXFP8 entry points: host-side sizes and argument errors (nothing is launched)."""
+    lib = _lib.load()
+    INV = _lib.MOE_ERR_INVALID_ARG
+    # token axis of a column copy: R + 31 E rounded up to 128
+    assert lib.moe_mx_col_len(100, 2) == 256
+    assert lib.moe_mx_col_len(131072, 32) == 132096
+    fake = ctypes.c_void_p(256)
+    good = _lib.MxT(256, 256, 64)
+    # n not a multiple of 32; ld smaller than n; misaligned codes
+    assert lib.moe_mx_quantize(fake, 1, 4, 48, ctypes.byref(good), None) == INV
+    assert lib.moe_mx_quantize(fake, 1, 4, 96, ctypes.byref(good), None) == INV
+    assert lib.moe_mx_quantize(fake, 1, 4, 64, ctypes.byref(_lib.MxT(258, 256, 64)), None) == INV
+    # transposed copy needs rows a multiple of 32
+    assert lib.moe_mx_quantize_transpose(fake, 1, 2, 48, 64, ctypes.byref(good), None) == INV
+    # gates without the row map / source rows
+    assert lib.moe_mx_quantize_experts(fake, 1, None, None, fake, 2, fake, fake, 4, 64, 64,
+                                       ctypes.byref(good), None, None) == INV
+    assert lib.moe_mx_quantize_experts(fake, 1, None, fake, fake, 2, fake, fake, 4, 64, 64,
+                                       ctypes.byref(good), None, None) == INV
+    # MXFP8 GEMM: K must be a multiple of 128; no bias
+    mx = _lib.MxT(256, 256, 96)
+    a = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), _lib.MOE_E4M3, None, None, None, 256, 4,
+                         64, 64, 96, 256, 0, ctypes.pointer(mx), ctypes.pointer(mx))
+    assert lib.moe_grouped_gemm_fwd(ctypes.byref(a), None) == INV
+    a = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), _lib.MOE_E4M3, None, None, fake, 256, 4,
+                         64, 64, 128, 256, 0, ctypes.pointer(good), ctypes.pointer(good))
+    assert lib.moe_grouped_gemm_fwd(ctypes.byref(a), None) == INV
+    # MXFP8 FC1: squared ReLU is not part of the MXFP8 variant
+    g = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _lib.MOE_E4M3, None, None, None, 256, 4, 64,
+                        128, 64, _lib.ACT["srelu"], 0.0, 1.0, 0, None, None, 0,
+                        ctypes.pointer(good), ctypes.pointer(good), None, None, None)
+    assert lib.moe_grouped_gemm_glu_fwd(ctypes.byref(g), None) == INV
+    # MXFP8 weight gradient without pad_offsets, or with a bias gradient
+    b = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_E4M3, _lib.MOE_BWD_WGRAD, None,
+                         None, None, 256, 4, 64, 64, 64, 256, None, 0, 0, ctypes.pointer(good),
+                         ctypes.pointer(good), None, None)
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
+
+
 def test_struct_layouts_match_header(tmp_path):
     """Field offsets and sizes of the ctypes structures equal the C compiler's."""
     import os
@@ -73,7 +113,8 @@ def test_struct_layouts_match_header(tmp_path):
     if cc is None:
         pytest.skip("no C compiler")
     structs = {"moe_glu_fwd_args_t": _lib.GluFwdArgs, "moe_gemm_fwd_args_t": _lib.GemmFwdArgs,
-               "moe_glu_bwd_args_t": _lib.GluBwdArgs, "moe_gemm_bwd_args_t": _lib.GemmBwdArgs}
+               "moe_glu_bwd_args_t": _lib.GluBwdArgs, "moe_gemm_bwd_args_t": _lib.GemmBwdArgs,
+               "moe_mx_t": _lib.MxT}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
     for cname, py in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')

@@ -238,3 +238,142 @@ def test_fullsize_sampled(name):
         report.update(_check_weight_grads(cfg, inp, L, idx, w, counts, offsets, row_map,
                                           experts, cols))
     print(name, {k: f"{v:.2e}" for k, v in report.items()}, flush=True)
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def _mx_err(g, o, bf16=False):
+    """(99.9th percentile, max) of |g - o| / rms(o) (bf16: beyond half an ulp)."""
+    from gpu_util import half_ulp_bf16, rms
+    g, o = np.asarray(g, np.float64), np.asarray(o, np.float64)
+    e = np.abs(g - o)
+    if bf16:
+        e = np.maximum(e - half_ulp_bf16(o), 0.0)
+    r = rms(o)
+    return float(np.quantile(e, 0.999)) / r, float(e.max()) / r
+
+
+class ChainMX:
+    """The oracle's MXFP8 chain (every GEMM operand QDQ'd in blocks of 32 along
+    its reduction axis; A and dH from exact values; dY = w dOut) evaluated for
+    chosen tokens and weight-gradient columns, one expert at a time."""
+
+    def __init__(self, cfg, inp, idx, w, offsets, pad, src_row):
+        from oracle import mx as omx
+        self.q = omx
+        self.cfg, self.idx, self.w = cfg, idx, w
+        self.x = _f32(inp["x"])
+        self.W1 = inp["W1"]
+        self.W2 = inp["W2"]
+        self.dout = _f32(inp["dOut"])
+        self.off, self.pad, self.src = offsets, pad, src_row
+
+    def weights(self, e):
+        f = self.cfg.f
+        W1 = _f32(self.W1[e]).astype(np.float64)
+        W2 = _f32(self.W2[e]).astype(np.float64)
+        return dict(w1d=self.q.mx_qdq(W1, 1), w1f=self.q.mx_qdq(W1, 0),
+                    w2f=self.q.mx_qdq(W2, 1), w2d=self.q.mx_qdq(W2, 0))
+
+    def tokens(self, toks):
+        cfg, f, q = self.cfg, self.cfg.f, self.q
+        out = {t: np.zeros(cfg.d) for t in toks}
+        dX = {t: np.zeros(cfg.d) for t in toks}
+        for e in sorted({int(self.idx[t, j]) for t in toks for j in range(cfg.k)}):
+            W = self.weights(e)
+            for t in toks:
+                for j in range(cfg.k):
+                    if int(self.idx[t, j]) != e:
+                        continue
+                    H = q.mx_qdq(self.x[t:t + 1].astype(np.float64), 1) @ W["w1d"].T
+                    A = om.glu_forward(H[:, :f], H[:, f:], cfg.act)
+                    Y = om.round_bf16(q.mx_qdq(A, 1) @ W["w2f"].T)[0]
+                    out[t] += self.w[t, j] * Y
+                    dY = self.w[t, j] * self.dout[t:t + 1].astype(np.float64)
+                    dA = q.mx_qdq(dY, 1) @ W["w2d"]
+                    Hs = om.round_bf16(H)
+                    dg, dl = om.glu_backward(dA, Hs[:, :f], Hs[:, f:], cfg.act)
+                    dH = np.concatenate([dg, dl], 1)
+                    dX[t] += om.round_bf16(q.mx_qdq(dH, 1) @ W["w1f"])[0]
+        return out, dX
+
+    def wgrad_cols(self, e, cols):
+        """dW2[e][:, j] and canonical dW1[e] rows j (gate) and f + j (linear)."""
+        cfg, f, q = self.cfg, self.cfg.f, self.q
+        s, u = int(self.off[e]), int(self.off[e + 1])
+        rows = self.src[s:u]
+        W = self.weights(e)
+        X = self.x[rows].astype(np.float64)
+        Hx = q.mx_qdq(X, 1)
+        # gate of each routed row (a token reaches expert e through one slot)
+        wr_rows = np.array([self.w[t, int(np.nonzero(self.idx[t] == e)[0][0])] for t in rows])
+        dY = wr_rows[:, None] * self.dout[rows].astype(np.float64)
+        tq = lambda v: _tok_qdq(q, v)
+        dYc = tq(dY)
+        Xc = tq(X)
+        dYr = q.mx_qdq(dY, 1)
+        res = {}
+        for j in cols:
+            H2 = Hx @ W["w1d"][[j, f + j]].T            # gate j, linear j for every row
+            A = om.glu_forward(H2[:, :1], H2[:, 1:], cfg.act)
+            res[("dW2", j)] = dYc.T @ tq(A)[:, 0]
+            dA = dYr @ W["w2d"][:, j]
+            Hs = om.round_bf16(H2)
+            dg, dl = om.glu_backward(dA[:, None], Hs[:, :1], Hs[:, 1:], cfg.act)
+            res[("dW1g", j)] = tq(dg)[:, 0] @ Xc
+            res[("dW1l", j)] = tq(dl)[:, 0] @ Xc
+        return res
+
+
+def _tok_qdq(q, v):
+    """QDQ of one expert's rows [c, n] along the tokens, blocks from the first row."""
+    c = v.shape[0]
+    cp = (c + 31) // 32 * 32
+    buf = np.zeros((cp,) + v.shape[1:])
+    buf[:c] = v
+    return q.mx_qdq(buf, 0)[:c]
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_mxfp8_sampled():
+    """dsv3_mxfp8_fwdbwd at full size: sampled token rows of out and dX, and
+    weight-gradient columns of a heavy and a light expert, against the
+    oracle's MXFP8 chain; routing, offsets and padded offsets bit-exact."""
+    cfg = synth.WORKLOADS["dsv3_mxfp8_fwdbwd"]
+    note(f"full-size {cfg.name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    from ragged_grouped_gemm_amd import ops
+    from ragged_grouped_gemm_amd.layer import MoEFFN
+    inp = synth.make_inputs(cfg)
+    t = lambda a: synth.to_torch(a, "cuda")
+    x, lg, dout = t(inp["x"]), t(inp["logits"]), t(inp["dOut"])
+    W1p, _ = ops.moe_repack_glu_weights(t(inp["W1"]))
+    Wm = MoEFFN.mx_weights(W1p, t(inp["W2"]))
+    del W1p
+    L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, score=cfg.score, normalize=cfg.normalize,
+               gemm="mxfp8")
+    L.forward(x, lg, Wm, None)
+    L.backward(dout, lg, Wm, None)
+    torch.cuda.synchronize()
+    idx, w, counts, offsets, row_map = _check_routing(cfg, inp, L)
+    pad = om.pad_offsets(counts)
+    np.testing.assert_array_equal(host(L.pad_offsets), pad)
+    toks, heavy, light = _sample_tokens(idx, counts, n_random=3, seed=cfg.seed)
+    ch = ChainMX(cfg, inp, idx, w, offsets, pad, host(L.src_row))
+    ref_out, ref_dx = ch.tokens(toks)
+    rep = {"out": _mx_err(host(L.out)[toks], np.stack([ref_out[k_] for k_ in toks]), bf16=True),
+           "dX": _mx_err(host(L.dX)[toks], np.stack([ref_dx[k_] for k_ in toks]), bf16=True)}
+    f = cfg.f
+    pos = om.glu_pack_rows(f, G)
+    cols = [0, f - 1]
+    for e in (heavy, light):
+        res = ch.wgrad_cols(e, cols)
+        for j in cols:
+            rep[f"dW2[{e}][:,{j}]"] = _mx_err(host(L.dW2[e, :, j]), res[("dW2", j)])
+            rep[f"dW1g[{e},{j}]"] = _mx_err(host(L.dW1p[e, int(pos[j])]), res[("dW1g", j)])
+            rep[f"dW1l[{e},{j}]"] = _mx_err(host(L.dW1p[e, int(pos[f + j])]), res[("dW1l", j)])
+    for e in range(cfg.E):
+        if counts[e] == 0:
+            assert not L.dW1p[e].any().item() and not L.dW2[e].any().item()
+    print(cfg.name, {k_: f"q999 {a:.2e} max {b:.2e}" for k_, (a, b) in rep.items()}, flush=True)
+    for name, (qv, mv) in rep.items():
+        assert mv <= 2e-2, (name, rep)
