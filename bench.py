@@ -67,14 +67,14 @@ def hbm_bytes(cfg):
            "permute": T * d * b + R * d * b + T * k * 4 + 8 * R,
            "combine": R * d * b + T * d * b + 8 * R}
     if cfg.gemm == "mxfp8":
-        # MXFP8 copies of Xp and dY, written straight from x / d_out: the rows
-        # are gathered once per copy (row and segment-column), codes + scales out
+        # MXFP8 copies of Xp and dY, written straight from x / d_out: each
+        # routed row is gathered once, both copies (codes + scales) written
         mxb = lambda n: R * n + R * n // 32
         out["permute"] = T * k * 4 + 12 * R
-        out["quantize_x"] = 2 * R * d * b + 2 * mxb(d)
+        out["quantize_x"] = R * d * b + 2 * mxb(d)
     if cfg.backward:
         if cfg.gemm == "mxfp8":
-            out["quantize_dy"] = 2 * R * d * b + 2 * mxb(d) + 8 * R
+            out["quantize_dy"] = R * d * b + 2 * mxb(d) + 8 * R
         out.update({"combine_bwd": T * d * b + 2 * R * d * b + 12 * R,
                     "route_topk_bwd": T * E * 8 + T * k * 8,
                     "unpermute_dx": R * d * b + T * d * b + 4 * R})

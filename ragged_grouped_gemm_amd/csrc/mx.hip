@@ -67,72 +67,130 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-enum { COLS_SEGMENTS = 0, COLS_TRANSPOSE = 1 };
-
-// Column copies: a workgroup quantizes one group of 32 source rows for 256
-// columns, thread c holding column c (its 32 values come from 32 coalesced
-// row reads of the workgroup) and writing 32 contiguous code bytes.
-//  COLS_SEGMENTS: group g = tokens [32 g, 32 g + 32) of the padded expert
-//    segments; source row of token position p in segment e is
-//    src_row[offsets[e] + p - pad_offsets[e]] (zero past the segment end).
-//  COLS_TRANSPOSE: group g = rows [32 rb, 32 rb + 32) of matrix b of a batch
-//    [B, rows, n]; output row b n + c.
-template <class EL, int MODE>
+// Transposed copy of a batch [B, rows, n]: a workgroup quantizes one group of
+// 32 rows for 256 columns, thread c holding column c (its 32 values come from
+// 32 coalesced row reads of the workgroup) and writing 32 contiguous code
+// bytes of output row b n + c.  (Weights only: made once, outside the layer.)
+template <class EL>
 __global__ void __launch_bounds__(256)
-    mx_cols_kernel(const typename EL::storage* __restrict__ x, int n, int rows, int E,
-                   const int32_t* __restrict__ offsets, const int32_t* __restrict__ pad_offsets,
-                   const int32_t* __restrict__ src_row, const int32_t* __restrict__ row_map,
-                   const float* __restrict__ topk_w, int k, uint8_t* __restrict__ codes,
-                   uint8_t* __restrict__ scales, long long ld, long long ngroups) {
-  __shared__ long long s_src[32];
-  __shared__ float s_w[32];
-  const int tid = threadIdx.x;
-  const int c = blockIdx.x * 256 + tid;
+    mx_transpose_kernel(const typename EL::storage* __restrict__ x, int n, int rows,
+                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, long long ld,
+                        long long ngroups) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
   for (long long g = blockIdx.y; g < ngroups; g += gridDim.y) {
-    long long out_base;
-    int prow0;
-    if constexpr (MODE == COLS_SEGMENTS) {
-      prow0 = (int)(g * 32);
-      if (prow0 >= pad_offsets[E]) break;  // same for the whole workgroup
-      int lo = 0, hi = E;                  // largest e with pad_offsets[e] <= prow0
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pad_offsets[mid] <= prow0) lo = mid; else hi = mid;
-      }
-      if (tid < 32) {
-        const int r = offsets[lo] + prow0 - pad_offsets[lo] + tid;
-        const bool ok = r < offsets[lo + 1];
-        const long long sr = ok ? (src_row ? (long long)src_row[r] : r) : -1;
-        s_src[tid] = sr;
-        s_w[tid] = (ok && topk_w) ? row_gate(row_map, topk_w, k, sr, r) : 1.0f;
-      }
-      out_base = 0;
-    } else {
-      const int nrb = rows / 32;
-      const long long b = g / nrb;
-      prow0 = (int)(g - b * nrb) * 32;
-      if (tid < 32) {
-        s_src[tid] = b * rows + prow0 + tid;
-        s_w[tid] = 1.0f;
-      }
-      out_base = b * n;
-    }
-    __syncthreads();
+    const int nrb = rows / 32;
+    const long long b = g / nrb;
+    const int prow0 = (int)(g - b * nrb) * 32;
     if (c < n) {
       float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const long long sr = s_src[i];
-        float t = sr >= 0 ? ld1(x + sr * n + c) : 0.0f;
-        if (topk_w) t *= s_w[i];
-        v[i] = t;
-      }
+      for (int i = 0; i < 32; ++i) v[i] = ld1(x + (b * rows + prow0 + i) * n + c);
       uint32_t w[8];
       const uint32_t sc = mx_quant32(v, w);
-      u32x4* dst = reinterpret_cast<u32x4*>(codes + (out_base + c) * ld + prow0);
+      u32x4* dst = reinterpret_cast<u32x4*>(codes + (b * n + c) * ld + prow0);
       dst[0] = u32x4{w[0], w[1], w[2], w[3]};
       dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-      scales[(out_base + c) * (ld / 32) + prow0 / 32] = (uint8_t)sc;
+      scales[(b * n + c) * (ld / 32) + prow0 / 32] = (uint8_t)sc;
+    }
+  }
+}
+
+// Row and column copies of one group of 32 expert-ordered rows x 256 columns
+// in one pass.  The workgroup loads the tile with 16-byte loads (gathered rows,
+// gate product applied) into LDS, row stride 260 floats; thread t then
+// quantizes row t % 32 of 32-column block t / 32 into the row copy (rows of a
+// wave read one block of 32 different rows: distinct banks) and column t over
+// the 32 rows into the column copy (consecutive columns: distinct banks).
+constexpr int TILE_LD = 260;
+
+template <class EL>
+__global__ void __launch_bounds__(256)
+    mx_rowcol_kernel(const typename EL::storage* __restrict__ x, int n, int E,
+                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ pad_offsets,
+                     const int32_t* __restrict__ src_row, const int32_t* __restrict__ row_map,
+                     const float* __restrict__ topk_w, int k, uint8_t* __restrict__ rcodes,
+                     uint8_t* __restrict__ rscales, long long rld, uint8_t* __restrict__ ccodes,
+                     uint8_t* __restrict__ cscales, long long cld, long long ngroups) {
+  constexpr int V = EL::VEC;               // elements per 16-byte load
+  __shared__ float tile[32 * TILE_LD];
+  __shared__ long long s_src[32];
+  __shared__ float s_w[32];
+  __shared__ int s_row[32];                // routed row of tile row i (or -1)
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * 256;
+  for (long long g = blockIdx.y; g < ngroups; g += gridDim.y) {
+    const int prow0 = (int)(g * 32);
+    if (prow0 >= pad_offsets[E]) break;    // same for the whole workgroup
+    int lo = 0, hi = E;                    // largest e with pad_offsets[e] <= prow0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pad_offsets[mid] <= prow0) lo = mid; else hi = mid;
+    }
+    if (tid < 32) {
+      const int r = offsets[lo] + prow0 - pad_offsets[lo] + tid;
+      const bool ok = r < offsets[lo + 1];
+      const long long sr = ok ? (src_row ? (long long)src_row[r] : r) : -1;
+      s_src[tid] = sr;
+      s_row[tid] = ok ? r : -1;
+      s_w[tid] = (ok && topk_w) ? row_gate(row_map, topk_w, k, sr, r) : 1.0f;
+    }
+    __syncthreads();
+    // load: 32 rows x 256 columns, 16 bytes per thread per step
+    constexpr int PER_ROW = 256 / V;                 // loads per tile row
+    constexpr int STEPS = 32 * PER_ROW / 256;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int idx = st * 256 + tid;
+      const int i = idx / PER_ROW, cc = (idx % PER_ROW) * V;
+      float v[V];
+      const long long sr = s_src[i];
+      if (sr >= 0 && c0 + cc < n) {
+        unpack_chunk(*reinterpret_cast<const u32x4*>(x + sr * n + c0 + cc), v, EL());
+        if (topk_w) {
+#pragma unroll
+          for (int q = 0; q < V; ++q) v[q] *= s_w[i];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < V; ++q) v[q] = 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < V; q += 4)
+        *reinterpret_cast<f32x4*>(tile + i * TILE_LD + cc + q) =
+            f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
+    }
+    __syncthreads();
+    float v[32];
+    uint32_t w8[8];
+    // row copy: row t % 32, block t / 32
+    {
+      const int i = tid & 31, b = tid >> 5, col = c0 + 32 * b;
+      const int r = s_row[i];
+      if (rcodes && r >= 0 && col < n) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(tile + i * TILE_LD + 32 * b + 4 * q);
+          v[4 * q] = t[0];
+          v[4 * q + 1] = t[1];
+          v[4 * q + 2] = t[2];
+          v[4 * q + 3] = t[3];
+        }
+        const uint32_t sc = mx_quant32(v, w8);
+        u32x4* d = reinterpret_cast<u32x4*>(rcodes + (size_t)r * rld + col);
+        d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
+        d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+        rscales[(size_t)r * (rld / 32) + col / 32] = (uint8_t)sc;
+      }
+    }
+    // column copy: column t over the 32 rows
+    if (ccodes && c0 + tid < n) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = tile[i * TILE_LD + tid];
+      const uint32_t sc = mx_quant32(v, w8);
+      u32x4* d = reinterpret_cast<u32x4*>(ccodes + (size_t)(c0 + tid) * cld + prow0);
+      d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
+      d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+      cscales[(size_t)(c0 + tid) * (cld / 32) + prow0 / 32] = (uint8_t)sc;
     }
     __syncthreads();
   }
@@ -158,17 +216,28 @@ void launch_rows(const void* x, long long rows, int n, const int32_t* src_row,
                      topk_w, k, out->data, out->scale, (long long)out->ld);
 }
 
-template <class EL, int MODE>
-void launch_cols(const void* x, int n, int rows, int E, const int32_t* offsets,
-                 const int32_t* pad_offsets, const int32_t* src_row, const int32_t* row_map,
-                 const float* topk_w, int k, const moe_mx_t* out, long long ngroups,
-                 hipStream_t s) {
+template <class EL>
+void launch_transpose(const void* x, int n, int rows, const moe_mx_t* out, long long ngroups,
+                      hipStream_t s) {
   const int gx = (n + 255) / 256;
-  const int gy = (int)(ngroups < 1 ? 1 : (ngroups > 16384 ? 16384 : ngroups));
-  hipLaunchKernelGGL((mx_cols_kernel<EL, MODE>), dim3(gx, gy), dim3(256), 0, s,
-                     reinterpret_cast<const typename EL::storage*>(x), n, rows, E, offsets,
-                     pad_offsets, src_row, row_map, topk_w, k, out->data, out->scale,
-                     (long long)out->ld, ngroups);
+  const int gy = (int)(ngroups > 16384 ? 16384 : ngroups);
+  hipLaunchKernelGGL(mx_transpose_kernel<EL>, dim3(gx, gy), dim3(256), 0, s,
+                     reinterpret_cast<const typename EL::storage*>(x), n, rows, out->data,
+                     out->scale, (long long)out->ld, ngroups);
+}
+
+template <class EL>
+void launch_rowcol(const void* x, int n, int E, const int32_t* offsets, const int32_t* pad_offsets,
+                   const int32_t* src_row, const int32_t* row_map, const float* topk_w, int k,
+                   const moe_mx_t* row_out, const moe_mx_t* col_out, long long ngroups,
+                   hipStream_t s) {
+  const int gx = (n + 255) / 256;
+  const int gy = (int)(ngroups > 16384 ? 16384 : ngroups);
+  hipLaunchKernelGGL(mx_rowcol_kernel<EL>, dim3(gx, gy), dim3(256), 0, s,
+                     reinterpret_cast<const typename EL::storage*>(x), n, E, offsets, pad_offsets,
+                     src_row, row_map, topk_w, k, row_out ? row_out->data : nullptr,
+                     row_out ? row_out->scale : nullptr, row_out ? (long long)row_out->ld : 0LL,
+                     col_out->data, col_out->scale, (long long)col_out->ld, ngroups);
 }
 
 }  // namespace
@@ -204,12 +273,8 @@ moe_status_t moe_mx_quantize_transpose(const void* x, int dtype, int batches, in
   MOE_CHECK_ARG(groups == 0 || (x && aligned16(x)));
   if (groups == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == MOE_BF16)
-    launch_cols<BF16, COLS_TRANSPOSE>(x, n, rows, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                      0, out, groups, s);
-  else
-    launch_cols<F32, COLS_TRANSPOSE>(x, n, rows, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                     0, out, groups, s);
+  if (dtype == MOE_BF16) launch_transpose<BF16>(x, n, rows, out, groups, s);
+  else launch_transpose<F32>(x, n, rows, out, groups, s);
   return launch_status();
 }
 
@@ -230,18 +295,19 @@ moe_status_t moe_mx_quantize_experts(const void* x, int dtype, const int32_t* sr
   if (R == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool bf = dtype == MOE_BF16;
-  if (row_out) {
-    if (bf) launch_rows<BF16>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
-    else launch_rows<F32>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
-  }
   if (col_out) {
+    // both copies from one read of the rows
     const long long groups = moe_mx_col_len(R, E) / 32;
     if (bf)
-      launch_cols<BF16, COLS_SEGMENTS>(x, n, 0, E, offsets, pad_offsets, src_row, row_map,
-                                       topk_w, k, col_out, groups, s);
+      launch_rowcol<BF16>(x, n, E, offsets, pad_offsets, src_row, row_map, topk_w, k, row_out,
+                          col_out, groups, s);
     else
-      launch_cols<F32, COLS_SEGMENTS>(x, n, 0, E, offsets, pad_offsets, src_row, row_map, topk_w,
-                                      k, col_out, groups, s);
+      launch_rowcol<F32>(x, n, E, offsets, pad_offsets, src_row, row_map, topk_w, k, row_out,
+                         col_out, groups, s);
+  } else if (bf) {
+    launch_rows<BF16>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
+  } else {
+    launch_rows<F32>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
   }
   return launch_status();
 }
