@@ -744,6 +744,9 @@ __device__ __forceinline__ void glu_bwd_values(const uint16_t* __restrict__ Hrow
 // "memory" clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Wait until this wave's LDS reads have returned.
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave are
 // outstanding (expcnt and lgkmcnt left at their maxima, i.e. not waited on).
 template <int N>
@@ -755,6 +758,13 @@ __device__ __forceinline__ void vm_wait() {
 // Wait until at most `ahead` whole steps (PERW loads each) are still in flight.
 template <int PERW, int MAXAHEAD>
 __device__ __forceinline__ void vm_wait_steps(int ahead) {
+  static_assert(MAXAHEAD <= 3 && 3 * PERW <= 63, "vmcnt holds at most 63");
+  if constexpr (MAXAHEAD >= 3) {
+    if (ahead >= 3) {
+      vm_wait<3 * PERW>();
+      return;
+    }
+  }
   if constexpr (MAXAHEAD >= 2) {
     if (ahead >= 2) {
       vm_wait<2 * PERW>();
@@ -994,6 +1004,87 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    if constexpr (TL::SCHED == 2) {
+      // Ping-pong: wave group g (= wm, one wave per SIMD) alternates a memory
+      // phase (read every fragment of one k-step into registers) and a
+      // compute phase (that step's MFMAs from registers), the two groups one
+      // phase apart, so that on each SIMD one wave is always feeding the MFMA
+      // pipe.  Phase t: group 0 reads step t / 2 (t even) and computes step
+      // (t - 1) / 2 (t odd); group 1 one phase later.  Every wave ends every
+      // phase at a barrier, after its LDS reads have returned.  Both groups
+      // have read step j by the end of phase 2 j + 1, so step j + S is loaded
+      // into step j's slot at the start of phase 2 j + 2; the loads of step
+      // j + 1 are waited for at the end of phase 2 j + 1.
+      static_assert(C::WGM == 2 && !MX, "ping-pong needs two wave groups");
+      const int grp = wm;
+#pragma unroll
+      for (int st = S_ - 1; st < S_; ++st)
+        if (st < nk) {
+          la.issue(stage_ptr(st), cur.kb0 + st * BK);
+          lb.issue(stage_ptr(st) + BM * CPR, cur.kb0 + st * BK);
+        }
+      // step 0 landed; the loads of steps 1 .. min(S, nk) - 1 may still fly
+      vm_wait_steps<PERW, S_ - 1>(min(S_, nk) - 1);
+      lds_barrier();
+      u32x4 fa[SUB][TM], fb[SUB][TN];
+      auto mem = [&](int j) {  // every fragment of step j into registers
+        const u32x4* As = stage_ptr(j);
+        const u32x4* Bs = As + BM * CPR;
+#pragma unroll
+        for (int s2 = 0; s2 < SUB; ++s2) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            fa[s2][i] = Frag<AKM, EL, BM, BKB>::load(As, wm * C::WTM + 32 * i, s2, lane);
+#pragma unroll
+          for (int jj = 0; jj < TN; ++jj)
+            fb[s2][jj] = Frag<BKM, EL, BN, BKB>::load(Bs, wn * C::WTN + 32 * jj, s2, lane);
+        }
+      };
+      auto comp = [&]() {      // that step's MFMAs
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s2 = 0; s2 < SUB; ++s2)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj) mma(acc[i][jj], fb[s2][jj], fa[s2][i], EL());
+        __builtin_amdgcn_s_setprio(0);
+      };
+      auto end_even = [&]() {  // end of phase 2 j (or 2 j + 2)
+        lds_wait();
+        lds_barrier();
+      };
+      auto end_odd = [&](int j) {  // end of phase 2 j + 1
+        lds_wait();
+        // step j + 1 must have landed; steps up to j + S - 1 may still fly
+        vm_wait_steps<PERW, S_ - 2>(min(S_ - 2, nk - 2 - j));
+        lds_barrier();
+        if (j + S_ < nk) {  // both groups have read step j: refill its slot
+          u32x4* nb = stage_ptr(j + S_);
+          la.issue(nb, cur.kb0 + (j + S_) * BK);
+          lb.issue(nb + BM * CPR, cur.kb0 + (j + S_) * BK);
+        }
+      };
+      // group 0: read step j in phase 2 j, compute it in 2 j + 1; group 1 one
+      // phase later.  Both pass the same 2 nk + 1 barriers.
+      if (grp == 0) {
+        for (int j = 0; j < nk; ++j) {
+          mem(j);
+          end_even();
+          comp();
+          end_odd(j);
+        }
+        end_even();
+      } else {
+        end_even();
+        for (int j = 0; j < nk; ++j) {
+          mem(j);
+          end_odd(j);
+          comp();
+          end_even();
+        }
+      }
+    } else
     for (int kt = 0; kt < nk; ++kt) {
       // loads issued after step kt's: steps kt+1 .. min(kt+S-2, nk-1)
       vm_wait_steps<PERW, S_ - 2>(min(S_ - 2, nk - 1 - kt));
@@ -1236,15 +1327,20 @@ moe_status_t launch_gemm(const GemmArgs& p, int max_cus, hipStream_t s) {
 }
 
 // Tile policies.  Large bf16 problems take 256 x 256 tiles with a two-stage
-// ring of 128-byte k-steps (64 KB each) and the pinned MFMA / LDS-read
-// interleave: 16 waves in a 4 x 4 grid (64 x 64 per wave) for the plain
-// epilogue, 8 waves in 2 x 4 (128 x 64 per wave) for the gated epilogues,
-// whose extra registers do not fit under the 16-wave limit of 128 VGPRs.
-// Small or narrow problems take 128 x 128, fp32 takes 64 x 128.
+// ring of 128-byte k-steps (64 KB each):
+//  - plain epilogue, both operands K-contiguous (FC2): 16 waves in a 4 x 4
+//    grid (64 x 64 per wave) with the pinned MFMA / LDS-read interleave;
+//  - plain epilogue with an MN-contiguous B (dgrads, weight gradients): 8
+//    waves in two ping-pong groups (128 x 64 per wave);
+//  - gated epilogues: 8 waves in 2 x 4 with the pinned interleave (their
+//    extra registers do not fit under the 16-wave limit of 128 VGPRs).
+// Each choice is the fastest of a same-process sweep at the DeepSeek-V3-like
+// shard.  Small or narrow problems take 128 x 128, fp32 takes 64 x 128.
 // MOE_GEMM_TILE=<n> in the environment selects variant n of the list below
 // for bf16 instead (tuning sweeps).
 typedef Tile<256, 256, 4, 4, 128, 2, 1> TBig;
 typedef Tile<256, 256, 2, 4, 128, 2, 1> TBigGlu;
+typedef Tile<256, 256, 2, 4, 128, 2, 2> TBigPingPong;
 typedef Tile<128, 128, 2, 2, 128, 2> TSmall;
 typedef Tile<64, 128, 2, 2, 128, 2> TF32;
 
@@ -1265,12 +1361,15 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
         case 1: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu>(p, max_cus, s);
         case 2: return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 4, 4, 128, 2, 0>>(p, max_cus, s);
         case 3: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall>(p, max_cus, s);
+        case 4: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigPingPong>(p, max_cus, s);
         default: break;
       }
     }
     if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall>(p, max_cus, s);
     if constexpr (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))
       return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu>(p, max_cus, s);
+    else if constexpr (!BKM)
+      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigPingPong>(p, max_cus, s);
     else return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig>(p, max_cus, s);
   }
 }
