@@ -349,3 +349,59 @@ def test_unpermute_of_permute_is_exact_multiple(k):
     s = ops.moe_unpermute_combine(xp, rm, None)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(s), k * host(xd))
+
+
+# ------------------------------------------------------------------ maximum sizes
+
+@pytest.mark.parametrize("T,E,k", [(300, 1024, 32), (200, 32, 32), (500, 1024, 1)])
+def test_route_and_permute_max_sizes(T, E, k):
+    """E = MOE_MAX_EXPERTS and k = MOE_MAX_TOPK (and k = E): routing and the
+    permutation bit-exact."""
+    note(f"route+permute max sizes T={T} E={E} k={k}")
+    rng = np.random.default_rng(T + E + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[::4] = np.round(lg[::4] * 2) / 2          # ties
+    for score in ("softmax", "sigmoid"):
+        idx_o, w_o, _ = om.route_topk(lg, k, score, True)
+        idx, w = ops.moe_route_topk(dev(lg), k, score, True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(idx), idx_o)
+        assert f32_ok(host(w), w_o)
+    counts, off, row_map, src_row = om.permute_indices(idx_o, E)
+    c, o, po, rm, sr, _ = ops.moe_permute(None, dev(idx_o.astype(np.int32)), E, gather=False,
+                                          want_pad=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(c), counts)
+    np.testing.assert_array_equal(host(o), off)
+    np.testing.assert_array_equal(host(po), om.pad_offsets(counts))
+    np.testing.assert_array_equal(host(rm), row_map)
+    np.testing.assert_array_equal(host(sr), src_row)
+
+
+def test_gemms_with_max_experts():
+    """1024 experts, most of them empty, the rest with 1-40 rows: FC1 + GLU, the
+    dgrad and the weight gradient against the oracle (empty experts exact zeros)."""
+    note("gemms with E = 1024")
+    rng = np.random.default_rng(1024)
+    E, d, f = 1024, 128, 64
+    counts = np.where(rng.random(E) < 0.7, 0, rng.integers(1, 41, E)).astype(np.int64)
+    counts[-1] = 33
+    rng, off, doff = _setup(list(counts), 9)
+    R = int(off[-1])
+    x64, xd = rand_bf16(rng, (R, d))
+    w64, wd = rand_bf16(rng, (E, 2 * f, d), d ** -0.5)
+    a, h = ops.moe_grouped_gemm_glu_fwd(xd, wd, doff)
+    g64, gd = rand_bf16(rng, (R, 2 * f))
+    da = ops.moe_grouped_gemm_bwd(gd, doff, mode="dgrad", w=wd)
+    dw, _ = ops.moe_grouped_gemm_bwd(gd, doff, mode="wgrad", a=xd)
+    torch.cuda.synchronize()
+    H = om.grouped_linear(x64, w64, off)
+    assert bf16_excess(host(h), H) <= 5e-3
+    pos = om.glu_pack_rows(f, G)
+    A = om.glu_forward(H[:, pos[:f]], H[:, pos[f:]], "swiglu")
+    assert bf16_excess(host(a), A) <= 5e-3
+    assert bf16_excess(host(da), om.grouped_dgrad(g64, w64, off)) <= 5e-3
+    ref_dw = om.grouped_wgrad(g64, x64, off)
+    got = host(dw)
+    assert f32_ok(got, ref_dw)
+    assert not np.any(got[counts == 0])
