@@ -40,6 +40,9 @@ def parse():
                     help="tokens of the workload the CPU oracle runs (bounded sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--permute", choices=["fused", "copy"], default="fused",
+                    help="bf16 / fp32 workloads: FC1 and FC1 wgrad read x through src_row "
+                         "(fused) or a materialized permuted copy (copy)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -59,13 +62,15 @@ def gemm_flops(cfg):
     return fl
 
 
-def hbm_bytes(cfg):
+def hbm_bytes(cfg, fused_permute=False):
     """Algorithmic bytes of the memory-bound kernels (each tensor read or written once)."""
     b = 4 if cfg.dtype == "f32" else 2
     T, R, d, k, E = cfg.T, cfg.R, cfg.d, cfg.k, cfg.E
     out = {"route_topk": T * E * 4 + T * k * 8,
            "permute": T * d * b + R * d * b + T * k * 4 + 8 * R,
            "combine": R * d * b + T * d * b + 8 * R}
+    if fused_permute:
+        out["permute"] = T * k * 4 + 12 * R     # routing indices only: no row is copied
     if cfg.gemm == "mxfp8":
         # MXFP8 copies of Xp and dY, written straight from x / d_out: each
         # routed row is gathered once, both copies (codes + scales) written
@@ -81,10 +86,11 @@ def hbm_bytes(cfg):
     return out
 
 
-def recorded_traffic(cfg, kernel):
+def recorded_traffic(cfg, kernel, permute):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, scaled by the copy calibration; None when there is no
-    record for this workload or the kernel source changed since it was taken."""
+    record for this workload and permute mode or the kernel source changed
+    since it was taken."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"traffic_grouped_gemm_{cfg.name}.json")
@@ -96,6 +102,8 @@ def recorded_traffic(cfg, kernel):
     except (OSError, KeyError, ValueError):
         return None
     if sha != rec.get("kernel_source_sha256") or kernel not in rec.get("kernels", {}):
+        return None
+    if rec.get("permute", "copy") != permute:
         return None
     return rec["kernels"][kernel]["traffic_bytes"]
 
@@ -176,7 +184,8 @@ def main():
     mx = cfg.gemm == "mxfp8"
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-               backward=cfg.backward, gemm=cfg.gemm)
+               backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused")
+    permute = "fused" if L.fuse_permute else "copy"
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
         # weights do not change between the synthetic steps)
@@ -211,7 +220,7 @@ def main():
         row = {"launches_per_step": n // args.steps, "ms": round(ms, 4)}
         if name in flops:
             row["tflops"] = round(flops[name] / ms / 1e9, 1)
-        hb = hbm_bytes(cfg).get(name)
+        hb = hbm_bytes(cfg, L.fuse_permute).get(name)
         if hb:
             row["gbs"] = round(hb / ms / 1e6, 1)
         kernels[name] = row
@@ -245,13 +254,14 @@ def main():
         "dtype": "f32" if cfg.dtype == "f32" else ("mxfp8" if mx else "bf16"), "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "k": cfg.k, "routed_rows": cfg.R, "score": cfg.score, "act": cfg.act,
+                   "permute": "mx_quantize_gather" if mx else permute,
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "gemm_only_tflops": round(total_flops / gemm_ms / 1e9, 2),
         "graph_ms_per_step": round(graph_ms, 4) if graph_ms else None,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(cfg, dom),
+                     "traffic": recorded_traffic(cfg, dom, permute),
                      "flop_per_launch": flops[dom], "ms_per_launch": round(per_op[dom][1], 4)},
         "kernels": kernels,
     }

@@ -210,6 +210,14 @@ typedef struct {
   moe_mx_t* a_row;
   moe_mx_t* a_col;
   const int32_t* pad_offsets;
+  /* Gather-fused permute (bf16 / float32; nullable, and must be NULL for
+   * MOE_E4M3, whose row copy is gathered by moe_mx_quantize_experts): with
+   * src_row from moe_permute, xp is the unpermuted x [src_rows, d] and row r
+   * of the product reads x[src_row[r]], so the permuted copy is never
+   * written.  x must span less than 2 GiB; rows whose index lies outside
+   * [0, src_rows) read as zeros. */
+  const int32_t* src_row;
+  int src_rows;
 } moe_glu_fwd_args_t;
 moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* args, void* stream);
 
@@ -296,6 +304,12 @@ typedef struct {
   const moe_mx_t* a_mx;
   const moe_mx_t* w_mx;
   const int32_t* pad_offsets;
+  /* WGRAD, gather-fused permute (bf16 / float32; nullable): with a_src_row
+   * from moe_permute, a is the unpermuted [a_src_rows, K] and row r of the
+   * segments reads a[a_src_row[r]] (FC1's weight gradient straight from x).
+   * Same limits as moe_glu_fwd_args_t.src_row. */
+  const int32_t* a_src_row;
+  int a_src_rows;
 } moe_gemm_bwd_args_t;
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream);
 

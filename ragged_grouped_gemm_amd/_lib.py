@@ -37,7 +37,8 @@ class GluFwdArgs(ctypes.Structure):
                 ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
                 ("alpha", c_float), ("gelu_tanh", c_int), ("h_out", c_void_p),
                 ("a_out", c_void_p), ("max_cus", c_int), ("xp_mx", _PMX), ("w1_mx", _PMX),
-                ("a_row", _PMX), ("a_col", _PMX), ("pad_offsets", c_void_p)]
+                ("a_row", _PMX), ("a_col", _PMX), ("pad_offsets", c_void_p),
+                ("src_row", c_void_p), ("src_rows", c_int)]
 
 
 class GemmFwdArgs(ctypes.Structure):
@@ -61,7 +62,8 @@ class GemmBwdArgs(ctypes.Structure):
                 ("a", c_void_p), ("w", c_void_p), ("offsets", c_void_p), ("E", c_int),
                 ("R", c_int), ("N", c_int), ("K", c_int), ("out", c_void_p), ("db", c_void_p),
                 ("accumulate", c_int), ("max_cus", c_int), ("g_mx", _PMX), ("a_mx", _PMX),
-                ("w_mx", _PMX), ("pad_offsets", c_void_p)]
+                ("w_mx", _PMX), ("pad_offsets", c_void_p), ("a_src_row", c_void_p),
+                ("a_src_rows", c_int)]
 
 
 _SIGS = {

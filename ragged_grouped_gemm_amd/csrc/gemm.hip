@@ -101,6 +101,11 @@ struct GemmArgs {
   int act, gelu_tanh;
   int accumulate;
   int gm;  // M-tiles per band of the tile order
+  // Gather-fused permute (nullable): RAGGED_M reads row r of A as row
+  // gather[r] of a; RAGGED_K reads k-row r of B as row gather[r] of b; the
+  // gathered source has gather_rows rows.
+  const int32_t* gather;
+  long long gather_rows;
   // MXFP8 operands (MX8): E8M0 scales of A and B, row strides in bytes
   const uint8_t* sa;
   const uint8_t* sb;
@@ -210,7 +215,7 @@ struct KGeom {
   }
 };
 
-template <class EL, int ROWS, int THREADS, int BKB>
+template <class EL, int ROWS, int THREADS, int BKB, bool GATHER = false>
 struct DmaK {
   typedef typename EL::storage S;
   typedef KGeom<BKB> Gm;
@@ -222,20 +227,36 @@ struct DmaK {
   int kc[PER];
   int K, Klo;
 
+  // GATHER: row r of the operand is row gidx[r] of X, which has grows rows
+  // (gather-fused permute); X then spans at most 2 GiB.
   __device__ __forceinline__ void setup(const S* X, long long ld, int r0, int rlim, int Kdim,
-                                        int tid, int Kmin = 0) {
+                                        int tid, int Kmin = 0, const int32_t* gidx = nullptr,
+                                        long long grows = 0) {
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X) + (size_t)r0 * ld, (short)0,
-                                           0x7ffffff0, 0x00020000);
     K = Kdim;
     Klo = Kmin;
+    if constexpr (GATHER) {
+      const long long bytes = grows * ld * (long long)sizeof(S);
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X), (short)0,
+                                             (int)(bytes > 0x7ffffff0LL ? 0x7ffffff0LL : bytes),
+                                             0x00020000);
+    } else {
+      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X) + (size_t)r0 * ld, (short)0,
+                                             0x7ffffff0, 0x00020000);
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       // lane l fills slot l % CPR of row l / CPR of this instruction's rows
       const int row = Gm::RPI * (w * PER + i) + lane / Gm::CPR;
       const int c = Gm::slot(row, lane % Gm::CPR);    // the chunk that belongs there
       kc[i] = c * EL::VEC;
-      voff[i] = (r0 + row < rlim) ? (uint32_t)(((size_t)row * ld + kc[i]) * sizeof(S)) : OOB;
+      if constexpr (GATHER) {
+        const int src = (r0 + row < rlim) ? gidx[r0 + row] : -1;
+        voff[i] = (src >= 0 && src < grows) ? (uint32_t)(((size_t)src * ld + kc[i]) * sizeof(S))
+                                            : OOB;
+      } else {
+        voff[i] = (r0 + row < rlim) ? (uint32_t)(((size_t)row * ld + kc[i]) * sizeof(S)) : OOB;
+      }
     }
   }
   __device__ __forceinline__ void issue(u32x4* stage, int k0) const {
@@ -256,7 +277,7 @@ struct DmaK {
 // ROWS values of mn.  For bf16, 16-byte chunk c of k-row k sits at slot
 // c ^ ((k & 3) << 2): the transposed fragment reads below touch 4 consecutive
 // k-rows x 64 bytes per half wave, which this spreads over distinct banks.
-template <class EL, int ROWS, int THREADS, int BKB>
+template <class EL, int ROWS, int THREADS, int BKB, bool GATHER = false>
 struct DmaMN {
   typedef typename EL::storage S;
   static constexpr int V = EL::VEC;
@@ -269,12 +290,31 @@ struct DmaMN {
   static constexpr bool SWZ = sizeof(S) == 2;
   static_assert(ROWB <= 1024 && INSTR % NW == 0, "tile does not split into wave loads");
   static_assert(!SWZ || ROWB % 256 == 0, "the bf16 swizzle needs 16 chunks per k-row");
+  static constexpr int KPW = PER * RPI;                 // consecutive k-rows per wave
+  typedef __attribute__((address_space(4))) const int32_t* CIdx;
   const S* X;
   long long ld;
   int c0, clim, kend, krl, slot;
+  // Gather-fused permute (GATHER): k-row k is row gidx[k] of X.  The
+  // source rows of the wave's KPW k-rows of the next step to be issued are
+  // read ahead with scalar loads (the same for every lane), so a step's DMA
+  // never waits on its index fetch; steps are issued in increasing order.
+  CIdx gidx;
+  __amdgpu_buffer_rsrc_t grs;
+  int gn;  // rows of X
+  int gi[KPW];
 
+  __device__ __forceinline__ void fetch_rows(int k0) {
+    const int base = k0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * KPW;
+#pragma unroll
+    for (int q = 0; q < KPW; ++q) gi[q] = gidx[max(min(base + q, kend - 1), 0)];
+  }
+
+  // Kmin: the first k of the first step (steps follow at BK intervals).
+  // gidx / grows: gathered source (rows of X), nullable.
   __device__ __forceinline__ void setup(const S* X_, long long ld_, int c0_, int clim_, int kend_,
-                                        int tid, int /*Kmin: every step starts in range*/ = 0) {
+                                        int tid, int Kmin = 0, const int32_t* gidx_ = nullptr,
+                                        long long grows = 0) {
     X = X_;
     ld = ld_;
     c0 = c0_;
@@ -283,9 +323,34 @@ struct DmaMN {
     const int lane = tid & 63;
     krl = (16 * lane) / ROWB;
     slot = ((16 * lane) % ROWB) / 16;
+    if constexpr (GATHER) {
+      gidx = (CIdx)gidx_;
+      long long bytes = (grows * ld - c0) * (long long)sizeof(S);
+      bytes = bytes < 0 ? 0 : (bytes > 0x7ffffff0LL ? 0x7ffffff0LL : bytes);
+      gn = (int)grows;
+      grs = __builtin_amdgcn_make_buffer_rsrc(const_cast<S*>(X) + c0, (short)0, (int)bytes,
+                                              0x00020000);
+      if (Kmin < kend) fetch_rows(Kmin);
+    }
   }
-  __device__ __forceinline__ void issue(u32x4* stage, int k0) const {
+  __device__ __forceinline__ void issue(u32x4* stage, int k0) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int kr = (w * PER + i) * RPI + krl;
+        const int chunk = SWZ ? (slot ^ ((kr & 3) << 2)) : slot;
+        int src = gi[i * RPI];
+#pragma unroll
+        for (int r = 1; r < RPI; ++r) src = krl == r ? gi[i * RPI + r] : src;
+        const bool ok = (k0 + kr < kend) && (c0 + chunk * V < clim) && src >= 0 && src < gn;
+        const uint32_t vo = ok ? (uint32_t)(((size_t)src * ld + chunk * V) * sizeof(S)) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, LDS_PTR(stage + (w * PER + i) * 64), 16,
+                                                 (int)vo, 0, 0, 0);
+      }
+      if (k0 + BK < kend) fetch_rows(k0 + BK);
+      return;
+    }
     __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<S*>(X) + (size_t)k0 * ld + c0, (short)0, 0x7ffffff0, 0x00020000);
 #pragma unroll
@@ -816,7 +881,7 @@ struct GemmCfg {
   static_assert(!MX || BKB == 128, "MX steps are 128 k (four scale blocks, one word)");
 };
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL>
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false>
 __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     grouped_gemm_kernel(GemmArgs p) {
   typedef GemmCfg<EL, EPI, TL> C;
@@ -947,10 +1012,13 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
   // the next tile's first loads before the epilogue was measured: it gains
   // nothing, and the ring position it needs costs more than that.)
   constexpr int BKB = C::BKB, SUB = C::SUB, CPR = BKB / 16;
-  typedef typename std::conditional<AKM, DmaK<EL, BM, THREADS, BKB>,
-                                    DmaMN<EL, BM, THREADS, BKB>>::type LoadA;
-  typedef typename std::conditional<BKM, DmaK<EL, BN, THREADS, BKB>,
-                                    DmaMN<EL, BN, THREADS, BKB>>::type LoadB;
+  // the gathered operand: A's rows (RAGGED_M) or B's k-rows (RAGGED_K)
+  constexpr bool GA = GATHER && GROUP == RAGGED_M, GB = GATHER && GROUP == RAGGED_K;
+  static_assert(!GATHER || (GA ? AKM : !BKM), "gathers whole K-rows or whole k-rows");
+  typedef typename std::conditional<AKM, DmaK<EL, BM, THREADS, BKB, GA>,
+                                    DmaMN<EL, BM, THREADS, BKB, GA>>::type LoadA;
+  typedef typename std::conditional<BKM, DmaK<EL, BN, THREADS, BKB, GB>,
+                                    DmaMN<EL, BN, THREADS, BKB, GB>>::type LoadB;
   constexpr int S_ = C::STAGES;
   constexpr bool MX = C::MX;
   static_assert(!MX || (AKM && BKM), "MXFP8 operands are K-contiguous");
@@ -972,8 +1040,13 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
   auto prologue = [&](const TileC& t) {
     const S* B = reinterpret_cast<const S*>(p.b);
     if constexpr (GROUP == RAGGED_M) B += (size_t)t.e * p.b_expert_stride;
-    la.setup(A, p.lda, t.m0, t.mlim, t.kend, tid, t.kbeg);
-    lb.setup(B, p.ldb, t.n0, p.N, t.kend, tid, t.kbeg);
+    if constexpr (GROUP == RAGGED_M) {
+      la.setup(A, p.lda, t.m0, t.mlim, t.kend, tid, t.kbeg, p.gather, p.gather_rows);
+      lb.setup(B, p.ldb, t.n0, p.N, t.kend, tid, t.kbeg);
+    } else {
+      la.setup(A, p.lda, t.m0, t.mlim, t.kend, tid, t.kbeg);
+      lb.setup(B, p.ldb, t.n0, p.N, t.kend, tid, t.kbeg, p.gather, p.gather_rows);
+    }
     if constexpr (MX) {
       const uint8_t* SB = p.sb;
       if constexpr (GROUP == RAGGED_M) SB += (size_t)t.e * p.sb_expert_stride;
@@ -1299,10 +1372,10 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
 
 // ------------------------------------------------------------------ launching
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL>
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false>
 moe_status_t launch_gemm(const GemmArgs& p, int max_cus, hipStream_t s) {
   typedef GemmCfg<EL, EPI, TL> C;
-  auto kern = grouped_gemm_kernel<EL, AKM, BKM, GROUP, EPI, TL>;
+  auto kern = grouped_gemm_kernel<EL, AKM, BKM, GROUP, EPI, TL, GATHER>;
   static int occ[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
@@ -1349,12 +1422,13 @@ inline int tile_variant() {
   return v ? atoi(v) : -1;
 }
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI>
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, bool GATHER = false>
 moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
   if constexpr (sizeof(typename EL::storage) == 4) {
-    return launch_gemm<EL, AKM, BKM, GROUP, EPI, TF32>(p, max_cus, s);
+    return launch_gemm<EL, AKM, BKM, GROUP, EPI, TF32, GATHER>(p, max_cus, s);
   } else {
-    constexpr bool kSweep = (EPI == EPI_STORE || EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
+    constexpr bool kSweep =
+        !GATHER && (EPI == EPI_STORE || EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
     if constexpr (kSweep) {
       switch (tile_variant()) {
         case 0: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig>(p, max_cus, s);
@@ -1365,12 +1439,12 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
         default: break;
       }
     }
-    if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall>(p, max_cus, s);
+    if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall, GATHER>(p, max_cus, s);
     if constexpr (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))
-      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu>(p, max_cus, s);
+      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu, GATHER>(p, max_cus, s);
     else if constexpr (!BKM)
-      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigPingPong>(p, max_cus, s);
-    else return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig>(p, max_cus, s);
+      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigPingPong, GATHER>(p, max_cus, s);
+    else return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig, GATHER>(p, max_cus, s);
   }
 }
 
@@ -1385,8 +1459,21 @@ moe_status_t dispatch_mx(const GemmArgs& p, bool big, int max_cus, hipStream_t s
   return launch_gemm<MX8, true, true, GROUP, EPI, TMxSmall>(p, max_cus, s);
 }
 
+// p.gather selects the gather-fused loaders, built for the gated forward
+// (rows of A) and the weight gradient (k-rows of B) only.
 template <bool AKM, bool BKM, int GROUP, int EPI>
 moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
+  constexpr bool kGather = (GROUP == RAGGED_M && AKM && epi_glu_fwd(EPI)) ||
+                           (GROUP == RAGGED_K && !BKM && EPI == EPI_STORE);
+  if constexpr (kGather) {
+    if (p.gather) {
+      if (dtype == MOE_BF16)
+        return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI, true>(p, big, max_cus, s);
+      return dispatch_tiles<F32, AKM, BKM, GROUP, EPI, true>(p, big, max_cus, s);
+    }
+  } else {
+    if (p.gather) return MOE_ERR_UNSUPPORTED;
+  }
   if (dtype == MOE_BF16) return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
   return dispatch_tiles<F32, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
 }
@@ -1417,6 +1504,20 @@ using namespace moe;
 
 // An MXFP8 GEMM operand with reduction length K: ld a multiple of 128 (whole
 // scale words per k-step) and at least K.
+// The gather index of an argument struct, or NULL when the caller's struct
+// predates the field.
+template <class A>
+inline const int32_t* gather_field(const A* a, const int32_t* const A::*f) {
+  const size_t end = (size_t)(reinterpret_cast<const char*>(&(a->*f)) -
+                              reinterpret_cast<const char*>(a)) + sizeof(const int32_t*) +
+                     sizeof(int);
+  return a->struct_size >= end ? a->*f : nullptr;
+}
+// A gathered source [rows, cols] must be addressable by 31-bit byte offsets.
+inline bool gather_fits(long long rows, long long cols, int dtype) {
+  return rows > 0 && rows * cols * (long long)dtype_size(dtype) <= 0x7ffffff0LL;
+}
+
 inline bool mx_in_ok(const moe_mx_t* m, long long K) {
   return m && m->data && m->scale && m->ld >= K && m->ld % 128 == 0 && aligned16(m->data) &&
          aligned16(m->scale);
@@ -1454,7 +1555,8 @@ inline void set_mx_out(GemmArgs& p, moe_mx_t* row, moe_mx_t* col, const int32_t*
 
 // MXFP8 FC1 + GLU (dtype == MOE_E4M3).
 moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
-  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_glu_fwd_args_t));
+  MOE_CHECK_ARG(a->struct_size >= offsetof(moe_glu_fwd_args_t, src_row));
+  MOE_CHECK_ARG(!gather_field(a, &moe_glu_fwd_args_t::src_row));
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU);
   MOE_CHECK_ARG(a->b1p == nullptr && a->d % 128 == 0);
   if (a->R == 0) return MOE_OK;
@@ -1534,7 +1636,8 @@ moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
 }
 
 moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
-  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_gemm_bwd_args_t));
+  MOE_CHECK_ARG(a->struct_size >= offsetof(moe_gemm_bwd_args_t, a_src_row));
+  MOE_CHECK_ARG(!gather_field(a, &moe_gemm_bwd_args_t::a_src_row));
   GemmArgs p = zero_args();
   p.E = a->E;
   if (a->mode == MOE_BWD_DGRAD) {
@@ -1608,6 +1711,11 @@ moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream)
   p.alpha = a->alpha;
   p.act = a->act;
   p.gelu_tanh = a->gelu_tanh;
+  if (const int32_t* g = gather_field(a, &moe_glu_fwd_args_t::src_row)) {
+    MOE_CHECK_ARG(gather_fits(a->src_rows, a->d, a->dtype));
+    p.gather = g;
+    p.gather_rows = a->src_rows;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool big = big_ragged_m(a->R, a->E, n1);
   if (a->act == MOE_ACT_SWIGLU)
@@ -1701,6 +1809,7 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
   p.E = a->E;
   p.R = a->R;
   if (a->mode == MOE_BWD_DGRAD) {
+    MOE_CHECK_ARG(!gather_field(a, &moe_gemm_bwd_args_t::a_src_row));
     if (a->R == 0) return MOE_OK;
     MOE_CHECK_ARG(a->w && aligned16(a->w));
     // da [R, K] = g [R, N] @ w[e] [N, K]:  GEMM M = rows, N' = K, K' = N
@@ -1729,6 +1838,11 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
   p.ldc = a->K;
   p.c_expert_stride = (long long)a->N * a->K;
   p.accumulate = a->accumulate;
+  if (const int32_t* g = gather_field(a, &moe_gemm_bwd_args_t::a_src_row)) {
+    MOE_CHECK_ARG(gather_fits(a->a_src_rows, a->K, a->dtype));
+    p.gather = g;
+    p.gather_rows = a->a_src_rows;
+  }
   moe_status_t st = dispatch<false, false, RAGGED_K, EPI_STORE>(
       a->dtype, p, big_ragged_k(a->R, a->E, a->N, a->K), a->max_cus, s);
   if (st != MOE_OK || !a->db) return st;

@@ -11,6 +11,11 @@ Backward: combine bwd (dY, dgate) -> route bwd (dlogits) -> FC2 dgrad + dGLU
 (dH) -> FC2 wgrad (dW2, db2) -> FC1 dgrad (dXp) -> FC1 wgrad (dW1p, db1p) ->
 unpermute-sum (dX).
 
+Gather-fused permute (``fuse_permute``, the default for bf16 / float32): the
+permuted copy Xp is never written; FC1 and FC1's weight gradient read each row
+of x through src_row, so the forward keeps a reference to x for the backward
+(x must not change in between).  ``fuse_permute=False`` materializes Xp.
+
 MXFP8 variant (``gemm="mxfp8"``): every GEMM operand is an MXFP8 copy blocked
 along that GEMM's reduction axis.  Xp and dY exist only as MXFP8 row and
 expert-segmented column copies written straight from x and d_out; FC1's
@@ -43,9 +48,11 @@ class MXWeights:
 class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
-                 backward=True, device="cuda", max_cus=0, gemm="bf16"):
+                 backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.mx = gemm == "mxfp8"
+        self.fuse_permute = fuse_permute and not self.mx
+        self.x_saved = None
         if self.mx and (bias or act == "srelu" or dtype != torch.bfloat16):
             raise ValueError("the MXFP8 variant is gated, bias-free, with bf16 activations")
         self.R = R = T * k
@@ -72,7 +79,7 @@ class MoEFFN:
         if self.mx:
             self._alloc_mx(z, dev)
             return
-        self.xp = z((R, d), dtype)
+        self.xp = None if self.fuse_permute else z((R, d), dtype)
         self.H = z((R, n1), dtype) if backward else None
         self.A = z((R, f), dtype)
         self.Y = z((R, d), dtype)
@@ -129,15 +136,18 @@ class MoEFFN:
         with self._op("route_topk"):
             ops.moe_route_topk(logits, self.k, self.score, self.normalize, self.topk_idx,
                                self.topk_w, self.err)
+        fused = self.fuse_permute
         with self._op("permute"):
             ops.moe_permute(x, self.topk_idx, self.E, counts=self.counts, offsets=self.offsets,
                             row_map=self.row_map, src_row=self.src_row, xp=self.xp, ws=self.ws,
-                            err_word=self.err)
+                            err_word=self.err, gather=not fused)
+        self.x_saved = x if fused else None
         with self._op("fc1_glu_fwd"):
-            ops.moe_grouped_gemm_glu_fwd(self.xp, W1p, self.offsets, b1p=b1p, act=self.act,
-                                         clamp=self.clamp, alpha=self.alpha,
+            ops.moe_grouped_gemm_glu_fwd(x if fused else self.xp, W1p, self.offsets, b1p=b1p,
+                                         act=self.act, clamp=self.clamp, alpha=self.alpha,
                                          gelu_tanh=self.gelu_tanh, save_h=self.H is not None,
-                                         h_out=self.H, a_out=self.A, max_cus=self.max_cus)
+                                         h_out=self.H, a_out=self.A, max_cus=self.max_cus,
+                                         src_row=self.src_row if fused else None)
         with self._op("fc2_fwd"):
             ops.moe_grouped_gemm_fwd(self.A, W2, self.offsets, b=b2, y=self.Y,
                                      max_cus=self.max_cus)
@@ -168,8 +178,13 @@ class MoEFFN:
             ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="dgrad", w=W1p, out=self.dXp,
                                      max_cus=self.max_cus)
         with self._op("fc1_wgrad"):
-            ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="wgrad", a=self.xp,
-                                     out=self.dW1p, db=self.db1p, max_cus=self.max_cus)
+            if self.fuse_permute:
+                ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="wgrad", a=self.x_saved,
+                                         a_src_row=self.src_row, out=self.dW1p, db=self.db1p,
+                                         max_cus=self.max_cus)
+            else:
+                ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="wgrad", a=self.xp,
+                                         out=self.dW1p, db=self.db1p, max_cus=self.max_cus)
         with self._op("unpermute_dx"):
             ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
         return self.dX

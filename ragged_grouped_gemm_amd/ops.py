@@ -190,9 +190,11 @@ def moe_repack_glu_weights(w, b=None, inverse=False, w_out=None, b_out=None):
 def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=0.0, alpha=1.0,
                              gelu_tanh=False, save_h=True, h_out=None, a_out=None, max_cus=0,
                              E=None, f=None, pad_offsets=None, a_row=None, a_col=None,
-                             want_row=True, want_col=True):
+                             want_row=True, want_col=True, src_row=None):
     """FC1 + GLU epilogue.  Returns (A [R, f], H [R, n1] or None).
 
+    src_row (gather-fused permute): xp is the unpermuted x [T, d] and row r
+    of the product reads x[src_row[r]] (R = src_row.numel()).
     MXFP8 operands (xp, w1p MXTensor row copies along d; E and f given):
     returns ((A row copy, A column copy), H bf16)."""
     if isinstance(xp, MXTensor):
@@ -214,7 +216,8 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
               "moe_grouped_gemm_glu_fwd")
         return ((a_row if want_row else None), (a_col if want_col else None)), \
             (h_out if save_h else None)
-    R, d = xp.shape
+    T, d = xp.shape
+    R = T if src_row is None else src_row.numel()
     E, n1, _ = w1p.shape
     f = n1 if act == "srelu" else n1 // 2
     a_out = _empty((R, f), xp.dtype, xp) if a_out is None else a_out
@@ -223,6 +226,9 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
     args = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _dtype(xp), _p(xp), _p(w1p), _p(b1p),
                            _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                            _p(h_out) if save_h else None, _p(a_out), max_cus)
+    if src_row is not None:
+        args.src_row = _p(src_row)
+        args.src_rows = T
     check(_lib.load().moe_grouped_gemm_glu_fwd(ctypes.byref(args), _stream()),
           "moe_grouped_gemm_glu_fwd")
     return a_out, (h_out if save_h else None)
@@ -284,8 +290,11 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
 
 def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None, want_db=False,
                          accumulate=False, max_cus=0, E=None, R=None, N=None, K=None,
-                         pad_offsets=None):
+                         pad_offsets=None, a_src_row=None):
     """mode "dgrad": da = g @ w[e];  mode "wgrad": dw[e] = g[seg]^T @ a[seg] (+ db).
+
+    a_src_row (wgrad, gather-fused permute): a is the unpermuted [T, K] and
+    row r of the segments reads a[a_src_row[r]].
 
     MXFP8 operands: dgrad takes g [R, N] row copy and w transposed [E*K, N]
     (E, K given; da bf16); wgrad takes g [N, L] and a [K, L] column copies
@@ -327,6 +336,9 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
         raise ValueError(mode)
     args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _dtype(g), m, _p(g), _p(a), _p(w),
                             _p(offsets), E, R, N, K, _p(out), _p(db), int(accumulate), max_cus)
+    if a_src_row is not None:
+        args.a_src_row = _p(a_src_row)
+        args.a_src_rows = a.shape[0]
     check(_lib.load().moe_grouped_gemm_bwd(ctypes.byref(args), _stream()),
           "moe_grouped_gemm_bwd")
     return (out, db) if mode == "wgrad" else out

@@ -104,6 +104,42 @@ def test_mx_host_checks():
     assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
 
 
+def test_gather_host_checks():
+    """Gather-fused permute arguments: where it is not built, and a source over
+    2 GiB, are refused before anything is launched."""
+    lib = _lib.load()
+    INV = _lib.MOE_ERR_INVALID_ARG
+    fake = 256
+    good = _lib.MxT(256, 256, 128)
+    # MXFP8 FC1 takes its rows from the quantizer: no src_row
+    g = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _lib.MOE_E4M3, None, None, None, fake, 4,
+                        64, 128, 64, _lib.ACT["swiglu"], 0.0, 1.0, 0, None, None, 0,
+                        ctypes.pointer(good), ctypes.pointer(good), None, None, None, fake, 64)
+    assert lib.moe_grouped_gemm_glu_fwd(ctypes.byref(g), None) == INV
+    # bf16 FC1 whose gathered source spans more than 2 GiB (2^20 rows x 1024 x 2 B)
+    g = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _lib.MOE_BF16, fake, fake, None, fake, 4,
+                        64, 1024, 64, _lib.ACT["swiglu"], 0.0, 1.0, 0, fake, fake, 0,
+                        None, None, None, None, None, fake, 1 << 20)
+    assert lib.moe_grouped_gemm_glu_fwd(ctypes.byref(g), None) == INV
+    # ... or no source rows at all
+    g.src_rows = 0
+    assert lib.moe_grouped_gemm_glu_fwd(ctypes.byref(g), None) == INV
+    # DGRAD has no gathered operand
+    b = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_BF16, _lib.MOE_BWD_DGRAD, fake,
+                         fake, fake, fake, 4, 64, 64, 64, fake, None, 0, 0, None, None, None,
+                         None, fake, 64)
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
+    # WGRAD source over 2 GiB
+    b.mode = _lib.MOE_BWD_WGRAD
+    b.a_src_rows = 1 << 24
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
+    # MXFP8 WGRAD: no gathered operand
+    b = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_E4M3, _lib.MOE_BWD_WGRAD, None,
+                         None, None, fake, 4, 64, 64, 128, fake, None, 0, 0, ctypes.pointer(good),
+                         ctypes.pointer(good), None, fake, fake, 64)
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
+
+
 def test_struct_layouts_match_header(tmp_path):
     """Field offsets and sizes of the ctypes structures equal the C compiler's."""
     import os

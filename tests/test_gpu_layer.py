@@ -66,12 +66,12 @@ def _device_inputs(cfg, inp):
     return x, lg, W1p, W2, b1p, b2, dout
 
 
-def _layer(cfg):
+def _layer(cfg, fused=False):
     from ragged_grouped_gemm_amd.layer import MoEFFN
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     return MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                   normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-                  backward=cfg.backward)
+                  backward=cfg.backward, fuse_permute=fused)
 
 
 def _oracle(cfg, inp):
@@ -98,13 +98,15 @@ def _pack_rows(a, cfg):
     return om.repack_glu(a, G=G, axis=1) if cfg.gated else a
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["xp", "fused_gather"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_layer_parity(name):
+def test_layer_parity(name, fused):
     cfg = CASES[name]
-    note(f"layer {name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k} {cfg.dtype} {cfg.act}")
+    note(f"layer {name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k} {cfg.dtype} {cfg.act}"
+         f" fused={fused}")
     inp = synth.make_inputs(cfg)
     x, lg, W1p, W2, b1p, b2, dout = _device_inputs(cfg, inp)
-    L = _layer(cfg)
+    L = _layer(cfg, fused)
     L.forward(x, lg, W1p, W2, b1p, b2)
     if cfg.backward:
         L.backward(dout, lg, W1p, W2)
@@ -118,7 +120,10 @@ def test_layer_parity(name):
     np.testing.assert_array_equal(host(L.offsets), fwd["offsets"])
     np.testing.assert_array_equal(host(L.row_map), fwd["row_map"])
     np.testing.assert_array_equal(host(L.src_row), fwd["src_row"])
-    np.testing.assert_array_equal(host(L.xp), fwd["xp"])
+    if fused:
+        assert L.xp is None          # the permuted copy is never written
+    else:
+        np.testing.assert_array_equal(host(L.xp), fwd["xp"])
     assert rel_l2(host(L.topk_w), fwd["topk_w"]) <= 1e-5
     assert int(L.err.item()) == 0
 
@@ -173,16 +178,38 @@ def test_layer_parity(name):
     print(name, {k: f"{v:.2e}" for k, v in report.items()}, flush=True)
 
 
-def test_graph_replay_matches_eager_and_is_deterministic():
+@pytest.mark.parametrize("name", ["dsv3_small", "mixtral_bigtile", "fp32_gated_clamp"])
+def test_fused_gather_layer_is_bit_identical(name):
+    """The gather-fused layer (no Xp) computes exactly what the layer with the
+    materialized Xp computes: only the rows' source addresses differ."""
+    cfg = CASES[name]
+    note(f"fused vs materialized permute {name}")
+    inp = synth.make_inputs(cfg)
+    x, lg, W1p, W2, b1p, b2, dout = _device_inputs(cfg, inp)
+    outs = []
+    for fused in (False, True):
+        L = _layer(cfg, fused)
+        L.forward(x, lg, W1p, W2, b1p, b2)
+        L.backward(dout, lg, W1p, W2)
+        outs.append(L)
+    torch.cuda.synchronize()
+    names = ["topk_idx", "row_map", "src_row", "H", "A", "Y", "out", "dY", "dH", "dXp", "dX",
+             "dgate", "dlogits", "dW1p", "dW2"] + (["db1p", "db2"] if cfg.bias else [])
+    for n in names:
+        assert torch.equal(getattr(outs[0], n), getattr(outs[1], n)), n
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["xp", "fused_gather"])
+def test_graph_replay_matches_eager_and_is_deterministic(fused):
     """One captured graph of the whole step, replayed with new routing inputs:
     every replay equals an eager run on the same inputs, bit for bit."""
     cfg = CASES["dsv3_small"]
-    note("graph replay dsv3_small")
+    note(f"graph replay dsv3_small fused={fused}")
     inp = synth.make_inputs(cfg)
     x, lg, W1p, W2, b1p, b2, dout = _device_inputs(cfg, inp)
-    Lg = _layer(cfg)
+    Lg = _layer(cfg, fused)
     graph = Lg.capture(x, lg, W1p, W2, dout)
-    Le = _layer(cfg)
+    Le = _layer(cfg, fused)
     seen_counts = []
     for seed in (11, 12, 13):
         new_lg = synth.draw_router(cfg.replace(seed=seed))
