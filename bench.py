@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--permute", choices=["fused", "copy"], default="fused",
                     help="bf16 / fp32 workloads: FC1 and FC1 wgrad read x through src_row "
                          "(fused) or a materialized permuted copy (copy)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="bf16 / fp32 training workloads: H is not kept from the forward, the "
+                         "backward runs FC1 + GLU again (its FLOP are not counted in the metric)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -184,7 +187,8 @@ def main():
     mx = cfg.gemm == "mxfp8"
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-               backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused")
+               backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
+               recompute=args.recompute)
     permute = "fused" if L.fuse_permute else "copy"
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
@@ -255,6 +259,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "k": cfg.k, "routed_rows": cfg.R, "score": cfg.score, "act": cfg.act,
                    "permute": "mx_quantize_gather" if mx else permute,
+                   "recompute_fc1": bool(args.recompute),
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "gemm_only_tflops": round(total_flops / gemm_ms / 1e9, 2),

@@ -1459,12 +1459,13 @@ moe_status_t dispatch_mx(const GemmArgs& p, bool big, int max_cus, hipStream_t s
   return launch_gemm<MX8, true, true, GROUP, EPI, TMxSmall>(p, max_cus, s);
 }
 
-// p.gather selects the gather-fused loaders, built for the gated forward
-// (rows of A) and the weight gradient (k-rows of B) only.
+// p.gather selects the gather-fused loaders, built for FC1's forward (rows
+// of A) and the weight gradient (k-rows of B) only.
 template <bool AKM, bool BKM, int GROUP, int EPI>
 moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
-  constexpr bool kGather = (GROUP == RAGGED_M && AKM && epi_glu_fwd(EPI)) ||
-                           (GROUP == RAGGED_K && !BKM && EPI == EPI_STORE);
+  constexpr bool kGather =
+      (GROUP == RAGGED_M && AKM && (epi_glu_fwd(EPI) || EPI == EPI_SRELU_FWD)) ||
+      (GROUP == RAGGED_K && !BKM && EPI == EPI_STORE);
   if constexpr (kGather) {
     if (p.gather) {
       if (dtype == MOE_BF16)

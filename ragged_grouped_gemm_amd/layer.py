@@ -16,6 +16,13 @@ permuted copy Xp is never written; FC1 and FC1's weight gradient read each row
 of x through src_row, so the forward keeps a reference to x for the backward
 (x must not change in between).  ``fuse_permute=False`` materializes Xp.
 
+Activation recomputation (``recompute=True``): the forward does not write
+the pre-activation H; the backward first runs FC1 + GLU again (from x or Xp,
+and the routing the forward left in place) to rebuild H and A, then proceeds
+as usual.  Between the passes the layer then needs only the routing, Y and
+its inputs, at the price of one more FC1 GEMM (4·R·d·f FLOP) per backward;
+the gradients are bit-identical to the stored-H path.
+
 MXFP8 variant (``gemm="mxfp8"``): every GEMM operand is an MXFP8 copy blocked
 along that GEMM's reduction axis.  Xp and dY exist only as MXFP8 row and
 expert-segmented column copies written straight from x and d_out; FC1's
@@ -48,9 +55,14 @@ class MXWeights:
 class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
-                 backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True):
+                 backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
+                 recompute=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         self.mx = gemm == "mxfp8"
+        if recompute and (self.mx or not backward):
+            raise ValueError("recompute applies to the bf16 / fp32 training layer")
+        self.recompute = recompute
+        self.W1p_saved = self.b1p_saved = None
         self.fuse_permute = fuse_permute and not self.mx
         self.x_saved = None
         if self.mx and (bias or act == "srelu" or dtype != torch.bfloat16):
@@ -142,12 +154,9 @@ class MoEFFN:
                             row_map=self.row_map, src_row=self.src_row, xp=self.xp, ws=self.ws,
                             err_word=self.err, gather=not fused)
         self.x_saved = x if fused else None
+        self.b1p_saved = b1p
         with self._op("fc1_glu_fwd"):
-            ops.moe_grouped_gemm_glu_fwd(x if fused else self.xp, W1p, self.offsets, b1p=b1p,
-                                         act=self.act, clamp=self.clamp, alpha=self.alpha,
-                                         gelu_tanh=self.gelu_tanh, save_h=self.H is not None,
-                                         h_out=self.H, a_out=self.A, max_cus=self.max_cus,
-                                         src_row=self.src_row if fused else None)
+            self._fc1(x, W1p, b1p, save_h=self.H is not None and not self.recompute)
         with self._op("fc2_fwd"):
             ops.moe_grouped_gemm_fwd(self.A, W2, self.offsets, b=b2, y=self.Y,
                                      max_cus=self.max_cus)
@@ -155,11 +164,23 @@ class MoEFFN:
             ops.moe_unpermute_combine(self.Y, self.row_map, self.topk_w, out=self.out)
         return self.out
 
+    def _fc1(self, x, W1p, b1p, save_h):
+        fused = self.fuse_permute
+        ops.moe_grouped_gemm_glu_fwd(x if fused else self.xp, W1p, self.offsets, b1p=b1p,
+                                     act=self.act, clamp=self.clamp, alpha=self.alpha,
+                                     gelu_tanh=self.gelu_tanh, save_h=save_h,
+                                     h_out=self.H if save_h else None, a_out=self.A,
+                                     max_cus=self.max_cus,
+                                     src_row=self.src_row if fused else None)
+
     def backward(self, d_out, logits, W1p, W2):
         if not self.has_backward:
             raise RuntimeError("layer built without backward buffers")
         if self.mx:
             return self._backward_mx(d_out, logits, W1p)
+        if self.recompute:
+            with self._op("fc1_recompute"):
+                self._fc1(self.x_saved, W1p, self.b1p_saved, save_h=True)
         with self._op("combine_bwd"):
             ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w, d_y=self.dY,
                                           d_topk_w=self.dgate)

@@ -66,12 +66,12 @@ def _device_inputs(cfg, inp):
     return x, lg, W1p, W2, b1p, b2, dout
 
 
-def _layer(cfg, fused=False):
+def _layer(cfg, fused=False, recompute=False):
     from ragged_grouped_gemm_amd.layer import MoEFFN
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     return MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                   normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-                  backward=cfg.backward, fuse_permute=fused)
+                  backward=cfg.backward, fuse_permute=fused, recompute=recompute)
 
 
 def _oracle(cfg, inp):
@@ -197,6 +197,32 @@ def test_fused_gather_layer_is_bit_identical(name):
              "dgate", "dlogits", "dW1p", "dW2"] + (["db1p", "db2"] if cfg.bias else [])
     for n in names:
         assert torch.equal(getattr(outs[0], n), getattr(outs[1], n)), n
+
+
+@pytest.mark.parametrize("name,fused", [("dsv3_small", True), ("dsv3_small", False),
+                                        ("mixtral_bigtile", True), ("fp32_gated_clamp", True),
+                                        ("srelu_small", False)])
+def test_recompute_is_bit_identical(name, fused):
+    """Recomputing FC1 in the backward (H not kept from the forward) gives
+    exactly the gradients of the layer that keeps H."""
+    cfg = CASES[name]
+    note(f"recompute vs saved H {name} fused={fused}")
+    inp = synth.make_inputs(cfg)
+    x, lg, W1p, W2, b1p, b2, dout = _device_inputs(cfg, inp)
+    Ls = _layer(cfg, fused)
+    Lr = _layer(cfg, fused, recompute=True)
+    for L in (Ls, Lr):
+        L.forward(x, lg, W1p, W2, b1p, b2)
+    torch.cuda.synchronize()
+    # the recomputing forward never writes H
+    assert not Lr.H.any() and Ls.H.any()
+    for L in (Ls, Lr):
+        L.backward(dout, lg, W1p, W2)
+    torch.cuda.synchronize()
+    names = ["out", "H", "A", "dY", "dH", "dXp", "dX", "dgate", "dlogits", "dW1p", "dW2"] + \
+        (["db1p", "db2"] if cfg.bias else [])
+    for n in names:
+        assert torch.equal(getattr(Ls, n), getattr(Lr, n)), n
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["xp", "fused_gather"])
