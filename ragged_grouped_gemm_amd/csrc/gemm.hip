@@ -626,6 +626,41 @@ __device__ __forceinline__ void epi_glu_bwd(const S* __restrict__ Hrow, S* __res
   }
 }
 
+// The same for bf16 H already in registers: h[g] = {gate, linear} bits of the
+// four values at A columns c0 + 8 g .. + 3.
+template <int ACT>
+__device__ __forceinline__ void epi_glu_bwd_raw(const u32x2 (&h)[4][2], uint16_t* __restrict__ Drow,
+                                                const f32x16& acc, int c0, int N, float L,
+                                                float alpha, int gtanh) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    if (col >= N) continue;
+    const int pg = (col >> 5) * 64 + (col & 31);
+    float dg[4], dl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wg = h[g][0][q >> 1], wl = h[g][1][q >> 1];
+      float gt = bf16_bits_to_f32((q & 1) ? (wg >> 16) : (wg & 0xffffu));
+      float li = bf16_bits_to_f32((q & 1) ? (wl >> 16) : (wl & 0xffffu));
+      float mg = 1.0f, ml = 1.0f;
+      if (L > 0.0f) {
+        mg = gt <= L ? 1.0f : 0.0f;
+        ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
+        gt = fminf(gt, L);
+        li = fminf(fmaxf(li, -L), L);
+      }
+      float a, da_dg;
+      act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
+      const float d = acc[4 * g + q];
+      dg[q] = d * li * da_dg * mg;
+      dl[q] = d * a * ml;
+    }
+    store4(Drow + pg, dg);
+    store4(Drow + pg + 32, dl);
+  }
+}
+
 // FC1 + squared ReLU (not gated): H = acc + b1, A = relu(min(H, L))^2.
 template <class S>
 __device__ __forceinline__ void epi_srelu_fwd(S* __restrict__ Hrow, S* __restrict__ Arow,
@@ -1326,6 +1361,43 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
             }
           }
         });
+      });
+    } else if constexpr (epi_glu_bwd(EPI) && sizeof(SO) == 2) {
+      // bf16 dGLU: the saved H of row block i + 1 (gate and linear values of
+      // every column block) is requested before row block i is computed and
+      // stored, so each block's load latency hides behind the previous block
+      // instead of stalling every block in turn.
+      u32x2 hr[2][TN][4][2];
+      const SO* Hbase = reinterpret_cast<const SO*>(p.aux);
+      auto hload = [&](int i, u32x2 (&buf)[TN][4][2]) {
+        const int row = m0 + wm * C::WTM + 32 * i + (lane & 31);
+        if (row < mlim) {
+          const SO* Hrow = Hbase + (size_t)row * p.ld_aux;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = cw + 32 * j + 8 * g;
+              const int pg = (col >> 5) * 64 + (col & 31);
+              if (col < p.N) {
+                buf[j][g][0] = *reinterpret_cast<const u32x2*>(Hrow + pg);
+                buf[j][g][1] = *reinterpret_cast<const u32x2*>(Hrow + pg + 32);
+              }
+            }
+        }
+      };
+      hload(0, hr[0]);
+      static_for<0, TM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < TM) hload(i + 1, hr[(i + 1) & 1]);
+        const int row = m0 + wm * C::WTM + 32 * i + (lane & 31);
+        if (row < mlim) {
+          SO* Drow = reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            epi_glu_bwd_raw<epi_act(EPI)>(hr[i & 1][j], Drow, acc[i][j], cw + 32 * j, p.N,
+                                          p.clamp, p.alpha, p.gelu_tanh);
+        }
       });
     } else
     static_for<0, TM>([&](auto ic) {
