@@ -59,7 +59,8 @@ Readings of points the pages leave open (each is listed in the design doc):
    block zero-padded) feed the weight gradients.  A and dH are quantized from
    their exact epilogue values, Xp from the stored x, dY from the product
    w * dOut; H stays a bf16 tensor for the backward epilogue.  Biases are not
-   part of the MXFP8 variant.
+   part of the MXFP8 variant.  The MXFP4 variant (``gemm="mxfp4"``) quantizes
+   the same tensors at the same points with E2M1 elements.
 """
 from __future__ import annotations
 
@@ -497,7 +498,8 @@ class LayerSpec:
         self.alpha = alpha
         self.gelu_tanh = gelu_tanh
         self.store = store      # dtype of every stored activation: "bf16", "f32" or "f64"
-        self.gemm = gemm        # GEMM operands: "bf16"/"f32" (the stored tensors) or "mxfp8"
+        self.gemm = gemm        # GEMM operands: "bf16"/"f32" (the stored tensors), "mxfp8"
+        #                         or "mxfp4" (same quantization points, E2M1 elements)
 
     @property
     def gated(self):
@@ -505,7 +507,12 @@ class LayerSpec:
 
     @property
     def mx(self):
-        return self.gemm == "mxfp8"
+        return self.gemm in ("mxfp8", "mxfp4")
+
+    @property
+    def fmt(self):
+        """Element format of the MX operands."""
+        return "e2m1" if self.gemm == "mxfp4" else "e4m3"
 
 
 def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
@@ -526,7 +533,8 @@ def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
         raise ValueError("the MXFP8 variant has no biases")
     pad = pad_offsets(counts) if q else None
     # FC1 reduces over d: activations and weights blocked along d
-    H = grouped_linear(_mx.mx_qdq(xp, 1) if q else xp, _mx.mx_qdq(_f64(W1), 2) if q else W1,
+    H = grouped_linear(_mx.mx_qdq(xp, 1, fmt=spec.fmt) if q else xp,
+                       _mx.mx_qdq(_f64(W1), 2, fmt=spec.fmt) if q else W1,
                        offsets, b1)
     if spec.gated:
         f = W1.shape[1] // 2
@@ -538,13 +546,15 @@ def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
     if q:
         # A from its exact values: row copy along f for FC2, column copy along
         # tokens for the FC2 weight gradient
-        A_fc2 = _mx.mx_qdq(A, 1)
-        res.update(A_row=A_fc2, A_col=_mx.mx_qdq_segments_colwise(A, offsets, pad),
-                   xp_col=_mx.mx_qdq_segments_colwise(xp, offsets, pad), pad_offsets=pad)
+        A_fc2 = _mx.mx_qdq(A, 1, fmt=spec.fmt)
+        res.update(A_row=A_fc2,
+                   A_col=_mx.mx_qdq_segments_colwise(A, offsets, pad, fmt=spec.fmt),
+                   xp_col=_mx.mx_qdq_segments_colwise(xp, offsets, pad, fmt=spec.fmt),
+                   pad_offsets=pad)
         A_s = A_fc2
     else:
         A_s = A_fc2 = rnd(A)
-    Y = grouped_linear(A_fc2, _mx.mx_qdq(_f64(W2), 2) if q else W2, offsets, b2)
+    Y = grouped_linear(A_fc2, _mx.mx_qdq(_f64(W2), 2, fmt=spec.fmt) if q else W2, offsets, b2)
     Y_s = rnd(Y)
     out = combine(Y_s, row_map, w)
     res.update(topk_idx=idx, topk_w=w, nan=nan, counts=counts, offsets=offsets,
@@ -567,10 +577,10 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
         pad = fwd["pad_offsets"]
         # dY from the product w * dOut: row copy along d (FC2 dgrad), column
         # copy along tokens (FC2 weight gradient); W2 blocked along d
-        dY_s = _mx.mx_qdq(dY, 1)
-        dY_col = _mx.mx_qdq_segments_colwise(dY, offsets, pad)
+        dY_s = _mx.mx_qdq(dY, 1, fmt=spec.fmt)
+        dY_col = _mx.mx_qdq_segments_colwise(dY, offsets, pad, fmt=spec.fmt)
         dW2, db2 = grouped_wgrad(dY_col, fwd["A_col"], offsets, with_bias=True)
-        dA = grouped_dgrad(dY_s, _mx.mx_qdq(_f64(W2), 1), offsets)
+        dA = grouped_dgrad(dY_s, _mx.mx_qdq(_f64(W2), 1, fmt=spec.fmt), offsets)
     else:
         dY_s = rnd(dY)
         dW2, db2 = grouped_wgrad(dY_s, fwd["A"], offsets, with_bias=True)
@@ -588,10 +598,10 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
         # multiple of 32 its blocks are the same in packed and canonical
         # order), column copy along tokens (FC1 weight gradient); W1 blocked
         # along 2f for the dgrad
-        dH_s = _mx.mx_qdq(dH, 1)
-        dH_col = _mx.mx_qdq_segments_colwise(dH, offsets, pad)
+        dH_s = _mx.mx_qdq(dH, 1, fmt=spec.fmt)
+        dH_col = _mx.mx_qdq_segments_colwise(dH, offsets, pad, fmt=spec.fmt)
         dW1, db1 = grouped_wgrad(dH_col, fwd["xp_col"], offsets, with_bias=True)
-        dXp = grouped_dgrad(dH_s, _mx.mx_qdq(_f64(W1), 1), offsets)
+        dXp = grouped_dgrad(dH_s, _mx.mx_qdq(_f64(W1), 1, fmt=spec.fmt), offsets)
     else:
         dH_s = rnd(dH)
         dW1, db1 = grouped_wgrad(dH_s, fwd["xp"], offsets, with_bias=True)

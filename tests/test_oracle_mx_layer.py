@@ -43,8 +43,34 @@ def qdq_last(v):
     return q.reshape(t.shape).numpy()
 
 
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def qdq_last_fp4(v):
+    """E2M1 QDQ along the last axis in blocks of 32: frexp scales (exponent of
+    amax minus 2) and the nearest of the eight E2M1 magnitudes by search (ties
+    to the even code), saturating at 6."""
+    t = np.asarray(v, dtype=np.float64)
+    n = t.shape[-1]
+    b = t.reshape(*t.shape[:-1], n // 32, 32)
+    amax = np.abs(b).max(-1, keepdims=True)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.where(amax > 0, np.clip(ex - 1 - 2, -127, 127), -127).astype(np.float64)
+    a = np.abs(b) / 2.0 ** e
+    d = np.abs(a[..., None] - E2M1_MAGS)                      # [..., 32, 8]
+    d = d + (np.arange(8) & 1) * 1e-12 * (d.min(-1, keepdims=True) + 1)   # ties: even code
+    m = E2M1_MAGS[np.argmin(d, axis=-1)]
+    m = np.where(a > 6.0, 6.0, m)
+    q = np.copysign(m, b) * 2.0 ** e
+    return q.reshape(t.shape)
+
+
+QLAST = {"e4m3": qdq_last, "e2m1": qdq_last_fp4}
+_fmt = ["e4m3"]
+
+
 def qdq_axis(v, axis):
-    return np.moveaxis(qdq_last(np.moveaxis(v, axis, -1)), -1, axis)
+    return np.moveaxis(QLAST[_fmt[0]](np.moveaxis(v, axis, -1)), -1, axis)
 
 
 def qdq_tokens(rows):
@@ -54,6 +80,10 @@ def qdq_tokens(rows):
     buf = np.zeros((cp, n))
     buf[:c] = rows
     return qdq_axis(buf, 0)[:c]
+
+
+def qlast(v):
+    return QLAST[_fmt[0]](v)
 
 
 def bf16(v):
@@ -76,9 +106,9 @@ def brute(x, logits, W1, W2, dout, spec):
             continue
         toks = [t for t, _ in assign]
         X = x[toks]
-        H = qdq_last(X) @ W1q_d[e].T
+        H = qlast(X) @ W1q_d[e].T
         A = om.glu_forward(H[:, :F], H[:, F:], spec.act)
-        Y = bf16(qdq_last(A) @ W2q_f[e].T)
+        Y = bf16(qlast(A) @ W2q_f[e].T)
         for r, (t, j) in enumerate(assign):
             Ys[(t, j)] = Y[r]
         per_expert[e] = (assign, X, bf16(H), A)
@@ -87,10 +117,10 @@ def brute(x, logits, W1, W2, dout, spec):
     for e, (assign, X, Hs, A) in per_expert.items():
         wr = np.array([w[t, j] for t, j in assign])
         dY = wr[:, None] * dout[[t for t, _ in assign]]
-        dA = qdq_last(dY) @ W2q_d[e]
+        dA = qlast(dY) @ W2q_d[e]
         dg, dl = om.glu_backward(dA, Hs[:, :F], Hs[:, F:], spec.act)
         dH = np.concatenate([dg, dl], 1)
-        dXp = bf16(qdq_last(dH) @ W1q_2f[e])
+        dXp = bf16(qlast(dH) @ W1q_2f[e])
         for r, (t, j) in enumerate(assign):
             dX[t] += dXp[r]
         dW2[e] = qdq_tokens(dY).T @ qdq_tokens(A)
@@ -107,12 +137,17 @@ def case():
     return cfg, f(inp["x"]), inp["logits"], f(inp["W1"]), f(inp["W2"]), f(inp["dOut"])
 
 
-def test_mx_chain_matches_brute_force(case):
+@pytest.mark.parametrize("gemm,fmt", [("mxfp8", "e4m3"), ("mxfp4", "e2m1")])
+def test_mx_chain_matches_brute_force(case, gemm, fmt):
     cfg, x, logits, W1, W2, dout = case
-    spec = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16", gemm="mxfp8")
+    spec = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16", gemm=gemm)
     fwd = om.layer_forward(x, logits, W1, W2, spec=spec)
     bwd = om.layer_backward(fwd, dout, logits, W1, W2, spec=spec)
-    ref = brute(x, logits, W1, W2, dout, spec)
+    _fmt[0] = fmt
+    try:
+        ref = brute(x, logits, W1, W2, dout, spec)
+    finally:
+        _fmt[0] = "e4m3"
     rel = lambda a, b: float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
     assert rel(fwd["out"], ref["out"]) < 1e-12
     assert rel(bwd["dX"], ref["dX"]) < 1e-12
@@ -120,13 +155,24 @@ def test_mx_chain_matches_brute_force(case):
     assert rel(bwd["dW2"], ref["dW2"]) < 1e-12
 
 
-def test_mx_chain_differs_from_plain_chain_by_quantization_size(case):
-    """The MX chain sits a few percent (E4M3 has 4 significant bits) from the
-    bf16 chain: far above fp64 noise, far below the signal."""
+def test_fp4_brute_force_qdq_agrees_with_torch_free_table():
+    """The brute-force E2M1 QDQ above, on values whose result the table fixes."""
+    v = np.zeros(32)
+    v[:8] = [6.0, 0.3, 0.75, 1.25, 2.6, -3.5, 5.0, -0.2]
+    np.testing.assert_array_equal(qdq_last_fp4(v)[:8], [6.0, 0.5, 1.0, 1.0, 3.0, -4.0, 4.0, -0.0])
+
+
+@pytest.mark.parametrize("gemm,lo,hi", [("mxfp8", 1e-3, 0.5), ("mxfp4", 2e-2, 0.6)])
+def test_mx_chain_differs_from_plain_chain_by_quantization_size(case, gemm, lo, hi):
+    """The MX chain sits a few percent (E4M3 has 4 significant bits; E2M1 two,
+    so tens of percent) from the bf16 chain: far above fp64 noise, below the
+    signal."""
     cfg, x, logits, W1, W2, dout = case
-    sp_mx = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16", gemm="mxfp8")
+    sp_mx = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16", gemm=gemm)
     sp_bf = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16")
     a = om.layer_forward(x, logits, W1, W2, spec=sp_mx)["out"]
     b = om.layer_forward(x, logits, W1, W2, spec=sp_bf)["out"]
-    r = om.norm_max_err(a, b)
-    assert 1e-3 < r < 0.5
+    # MXFP8: max error / rms; MXFP4 (one mantissa bit): rms error / rms
+    r = om.norm_max_err(a, b) if gemm == "mxfp8" else \
+        float(np.sqrt(np.mean((a - b) ** 2) / np.mean(b ** 2)))
+    assert lo < r < hi
