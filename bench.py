@@ -25,6 +25,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5033.2        # MI355X dense fp8 MFMA (MXFP8 operands)
+PEAK_FP4_TFLOPS = 10066.4       # MI355X dense fp4 MFMA (MXFP4 operands)
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE FFN fwd+bwd TFLOPS and % of MFMA peak, 1×MI355X"
@@ -74,14 +75,15 @@ def hbm_bytes(cfg, fused_permute=False):
            "combine": R * d * b + T * d * b + 8 * R}
     if fused_permute:
         out["permute"] = T * k * 4 + 12 * R     # routing indices only: no row is copied
-    if cfg.gemm == "mxfp8":
-        # MXFP8 copies of Xp and dY, written straight from x / d_out: each
-        # routed row is gathered once, both copies (codes + scales) written
-        mxb = lambda n: R * n + R * n // 32
+    if cfg.gemm in ("mxfp8", "mxfp4"):
+        # MX copies of Xp and dY, written straight from x / d_out: each routed
+        # row is gathered once, both copies (codes + scales) written
+        cb = 1.0 if cfg.gemm == "mxfp8" else 0.5           # code bytes per element
+        mxb = lambda n: int(R * n * cb) + R * n // 32
         out["permute"] = T * k * 4 + 12 * R
         out["quantize_x"] = R * d * b + 2 * mxb(d)
     if cfg.backward:
-        if cfg.gemm == "mxfp8":
+        if cfg.gemm in ("mxfp8", "mxfp4"):
             out["quantize_dy"] = R * d * b + 2 * mxb(d) + 8 * R
         out.update({"combine_bwd": T * d * b + 2 * R * d * b + 12 * R,
                     "route_topk_bwd": T * E * 8 + T * k * 8,
@@ -141,7 +143,8 @@ def cpu_baseline(cfg, inp, tokens):
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"first {Tc} of {cfg.T} tokens of {cfg.name} (R={Tc * cfg.k} routed rows), "
                       f"full expert weights, forward{'+backward' if cfg.backward else ''}, fp64"
-                      + (", MXFP8 QDQ of every GEMM operand" if cfg.gemm == "mxfp8" else "")}
+                      + (f", {cfg.gemm.upper()} QDQ of every GEMM operand"
+                         if cfg.gemm in ("mxfp8", "mxfp4") else "")}
 
 
 def main():
@@ -184,7 +187,7 @@ def main():
     else:
         W1p, b1p = W1, b1
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
-    mx = cfg.gemm == "mxfp8"
+    mx = cfg.gemm in ("mxfp8", "mxfp4")
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
@@ -193,7 +196,7 @@ def main():
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
         # weights do not change between the synthetic steps)
-        W1p = MoEFFN.mx_weights(W1p, W2)
+        W1p = MoEFFN.mx_weights(W1p, W2, cfg.gemm)
         W2 = None
     torch.cuda.synchronize()
 
@@ -231,6 +234,7 @@ def main():
     gemm_ms = sum(per_op[n][1] for n in flops)
     dom = max(flops, key=lambda n: per_op[n][1])
     peak = (PEAK_F32_TFLOPS if cfg.dtype == "f32" else
+            PEAK_FP4_TFLOPS if cfg.gemm == "mxfp4" else
             PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS)
     achieved = flops[dom] / per_op[dom][1] / 1e9
     value = total_flops / ms_step / 1e9
@@ -255,7 +259,8 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if cfg.dtype == "f32" else ("mxfp8" if mx else "bf16"), "data": "synthetic",
+        "dtype": "f32" if cfg.dtype == "f32" else (cfg.gemm if mx else "bf16"),
+        "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "f": cfg.f, "E": cfg.E,
                    "k": cfg.k, "routed_rows": cfg.R, "score": cfg.score, "act": cfg.act,
                    "permute": "mx_quantize_gather" if mx else permute,

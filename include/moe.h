@@ -71,12 +71,13 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_E4M3 = 2  /* MXFP8 GEMM operands (moe_mx_t); see the MXFP8 section below */
+  MOE_E4M3 = 2, /* MXFP8 GEMM operands (moe_mx_t); see the MXFP8 section below */
+  MOE_E2M1 = 3  /* MXFP4 GEMM operands (moe_mx_t, two codes per byte), same section */
 } moe_dtype_t;
 
-/* An MXFP8 matrix (layout and format in the MXFP8 section below). */
+/* An MXFP8 or MXFP4 matrix (layout and format in the MXFP8 section below). */
 typedef struct {
-  uint8_t* data;   /* E4M3 codes [rows, ld] */
+  uint8_t* data;   /* E4M3 codes [rows, ld] or E2M1 codes [rows, ld / 2] bytes */
   uint8_t* scale;  /* E8M0 codes [rows, ld / 32] */
   int64_t ld;      /* elements per row, a multiple of 32 */
 } moe_mx_t;
@@ -200,7 +201,7 @@ typedef struct {
   void* h_out;
   void* a_out;
   int max_cus;
-  /* dtype == MOE_E4M3: xp_mx [R, d] and w1_mx [E*n1, d] (row copies along
+  /* dtype == MOE_E4M3 or MOE_E2M1: xp_mx [R, d] and w1_mx [E*n1, d] (row copies along
    * d) replace xp / w1p; h_out stays bf16; A is written as a_row (row copy
    * [R, f], nullable) and a_col (column copy [f, moe_mx_col_len], nullable,
    * needs pad_offsets), quantized from the float32 epilogue values.  Gated
@@ -211,7 +212,7 @@ typedef struct {
   moe_mx_t* a_col;
   const int32_t* pad_offsets;
   /* Gather-fused permute (bf16 / float32; nullable, and must be NULL for
-   * MOE_E4M3, whose row copy is gathered by moe_mx_quantize_experts): with
+   * the MX dtypes, whose row copy is gathered by moe_mx_quantize_experts): with
    * src_row from moe_permute, xp is the unpermuted x [src_rows, d] and row r
    * of the product reads x[src_row[r]], so the permuted copy is never
    * written.  x must span less than 2 GiB; rows whose index lies outside
@@ -234,7 +235,7 @@ typedef struct {
   int E, R, N, K;
   void* y;
   int max_cus;
-  /* dtype == MOE_E4M3: a_mx [R, K] and w_mx [E*N, K] row copies replace a / w;
+  /* dtype == MOE_E4M3 or MOE_E2M1: a_mx [R, K] and w_mx [E*N, K] row copies replace a / w;
    * y is bf16; no bias. */
   const moe_mx_t* a_mx;
   const moe_mx_t* w_mx;
@@ -262,7 +263,7 @@ typedef struct {
   int gelu_tanh;
   void* dh;
   int max_cus;
-  /* dtype == MOE_E4M3: dy_mx [R, d] (row copy along d) and w2t_mx [E*f, d]
+  /* dtype == MOE_E4M3 or MOE_E2M1: dy_mx [R, d] (row copy along d) and w2t_mx [E*f, d]
    * (W2 transposed, blocked along d) replace dy / w2; h is bf16; dH is written
    * as dh_row (row copy [R, n1] in the packed layout, nullable) and dh_col
    * (column copy [n1, moe_mx_col_len], nullable, needs pad_offsets), quantized
@@ -295,7 +296,7 @@ typedef struct {
   float* db;           /* WGRAD, nullable */
   int accumulate;
   int max_cus;
-  /* dtype == MOE_E4M3:
+  /* dtype == MOE_E4M3 or MOE_E2M1:
    *   DGRAD: g_mx [R, N] row copy, w_mx [E*K, N] (w transposed, blocked along
    *          N); da is bf16.
    *   WGRAD: g_mx [N, L] and a_mx [K, L] column copies (L = moe_mx_col_len),
@@ -338,7 +339,17 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream)
  *    ld = K; blocked along N it is the transposed copy [E*K rows, ld = N].
  * MX GEMM operands need the reduction length (K, ld) a multiple of 128.
  * The layer's MXFP8 variant has no biases.  (moe_mx_t is declared beside the
- * element types above.) */
+ * element types above.)
+ *
+ * MXFP4 (dtype MOE_E2M1, the 4-bit variant; the pages' 4-bit format is NVFP4,
+ * whose E2M1 elements the CDNA4 matrix cores take with E8M0 scales per 32):
+ * the same layouts with E2M1 elements -- sign, 2 exponent bits, 1 mantissa
+ * bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 -- packed two per byte (element
+ * 2i in the low nibble of byte i, so a row holds ld / 2 bytes), block
+ * exponent e = floor(log2 amax) - 2, elements rounded to nearest even and
+ * saturated to +-6 (a NaN becomes +-6).  The GEMM entry points take MXFP4
+ * operands with dtype MOE_E2M1 and write their MX outputs (A, dH copies) in
+ * MXFP4 too; the moe_mxfp4_quantize* functions mirror the MXFP8 ones. */
 
 /* Length of the token axis of an expert-segmented column copy:
  * R + 31 E rounded up to a multiple of 128 (an upper bound of pad_offsets[E]). */
@@ -369,6 +380,18 @@ moe_status_t moe_mx_quantize_experts(const void* x, int dtype, const int32_t* sr
                                      const int32_t* offsets, const int32_t* pad_offsets, int E,
                                      int R, int n, moe_mx_t* row_out, moe_mx_t* col_out,
                                      void* stream);
+
+/* MXFP4 counterparts of the three quantizers above (same arguments; out,
+ * row_out, col_out receive E2M1 codes, ld / 2 bytes per row). */
+moe_status_t moe_mxfp4_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
+                                void* stream);
+moe_status_t moe_mxfp4_quantize_transpose(const void* x, int dtype, int batches, int rows, int n,
+                                          moe_mx_t* out, void* stream);
+moe_status_t moe_mxfp4_quantize_experts(const void* x, int dtype, const int32_t* src_row,
+                                        const int32_t* row_map, const float* topk_w, int k,
+                                        const int32_t* offsets, const int32_t* pad_offsets, int E,
+                                        int R, int n, moe_mx_t* row_out, moe_mx_t* col_out,
+                                        void* stream);
 
 /* ---------------------------------------------------------------- combine
  * a5 / a12.  out[t] = sum_{j=0..k-1} topk_w[t,j] * y[row_map[t,j]], summed in

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_E4M3, MOE_E2M1 = 0, 1, 2, 3
 ACT = {"swiglu": 0, "geglu": 1, "srelu": 2}
 SCORE = {"softmax": 0, "sigmoid": 1}
 MOE_BWD_DGRAD, MOE_BWD_WGRAD = 0, 1
@@ -94,6 +94,12 @@ _SIGS = {
     "moe_mx_quantize_experts": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                         c_void_p, c_void_p, c_int, c_int, c_int, _PMX, _PMX,
                                         c_void_p]),
+    "moe_mxfp4_quantize": (c_int, [c_void_p, c_int, ctypes.c_int64, c_int, _PMX, c_void_p]),
+    "moe_mxfp4_quantize_transpose": (c_int, [c_void_p, c_int, c_int, c_int, c_int, _PMX,
+                                             c_void_p]),
+    "moe_mxfp4_quantize_experts": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                           c_void_p, c_void_p, c_int, c_int, c_int, _PMX, _PMX,
+                                           c_void_p]),
 }
 
 _lib = None

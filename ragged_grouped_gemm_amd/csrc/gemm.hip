@@ -66,18 +66,37 @@ enum { RAGGED_M = 0, RAGGED_K = 1 };
 // 32 along K, multiplied by v_mfma_scale_f32_32x32x64_f8f6f4.  Both operands
 // are K-contiguous; outputs of these GEMMs are bf16 (or float32 for weight
 // gradients, or MXFP8 copies written by the epilogue).
+// MX operands: EPB k elements per storage byte, FMT the scaled MFMA's
+// operand format code (0 = E4M3, 4 = E2M1).  The loaders count K in bytes.
 struct MX8 {
   typedef uint8_t storage;
   static constexpr int VEC = 16;
+  static constexpr int EPB = 1, FMT = 0;
+  typedef FmtE4M3 Fmt;
+};
+struct MX4 {
+  typedef uint8_t storage;
+  static constexpr int VEC = 16;
+  static constexpr int EPB = 2, FMT = 4;
+  typedef FmtE2M1 Fmt;
 };
 template <class EL>
 constexpr bool is_mx() {
-  return std::is_same<EL, MX8>::value;
+  return std::is_same<EL, MX8>::value || std::is_same<EL, MX4>::value;
+}
+template <class EL>
+constexpr int epb() {
+  if constexpr (is_mx<EL>()) return EL::EPB;
+  else return 1;
 }
 // storage type of the GEMM's own outputs (C, saved H)
 template <class EL>
 struct OutT {
   typedef typename EL::storage type;
+};
+template <>
+struct OutT<MX4> {
+  typedef uint16_t type;
 };
 template <>
 struct OutT<MX8> {
@@ -469,7 +488,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // by the h = 0 lane's scale, block 1 by the h = 1 lane's (lane layout and
 // scale pairing measured on the device).  So the lane reads 16-byte chunks
 // 4 s + h and 4 s + 2 + h of its row.
-template <int ROWS, int BKB>
+template <int ROWS, int BKB, class EL = MX8>
 struct FragMX {
   static constexpr int READS = 2;
   __device__ __forceinline__ static u32x8 load(const u32x4* st, int r0, int s, int lane) {
@@ -478,6 +497,22 @@ struct FragMX {
     const u32x4 lo = st[row * Gm::CPR + Gm::slot(row, 4 * s + h)];
     const u32x4 hi = st[row * Gm::CPR + Gm::slot(row, 4 * s + 2 + h)];
     return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+};
+
+// MXFP4 fragment for k sub-step s (64 k = 32 bytes) of a 64-byte step: with
+// E2M1 operands the scaled MFMA reads 16 bytes per lane, lane half h holding
+// block h (k = 32 h .. 32 h + 31 of the sub-step) in its first four dwords
+// and ignoring the other four (measured on the device), so the lane reads
+// chunk 2 s + h of its row.
+template <int ROWS, int BKB>
+struct FragMX<ROWS, BKB, MX4> {
+  static constexpr int READS = 1;
+  __device__ __forceinline__ static u32x8 load(const u32x4* st, int r0, int s, int lane) {
+    typedef KGeom<BKB> Gm;
+    const int row = r0 + (lane & 31), h = lane >> 5;
+    const u32x4 c = st[row * Gm::CPR + Gm::slot(row, 2 * s + h)];
+    return u32x8{c[0], c[1], c[2], c[3], 0u, 0u, 0u, 0u};
   }
 };
 
@@ -494,14 +529,14 @@ __device__ __forceinline__ void mma(f32x16& acc, const u32x4& b, const u32x4& a,
                                                0, 0, 0);
 }
 
-// Scaled MXFP8 MFMA; the scale words carry the lane's block scale in byte
-// OPSEL (B first, as for bf16).
-template <int OPSEL>
+// Scaled MX MFMA (operand format FMT: 0 E4M3, 4 E2M1); the scale words
+// carry the lane's block scale in byte OPSEL (B first, as for bf16).
+template <int OPSEL, int FMT = 0>
 __device__ __forceinline__ void mma_mx(f32x16& acc, const u32x8& b, const u32x8& a, uint32_t sb,
                                        uint32_t sa) {
   acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, b),
-                                                        __builtin_bit_cast(i32x8, a), acc, 0, 0,
-                                                        OPSEL, (int)sb, OPSEL, (int)sa);
+                                                        __builtin_bit_cast(i32x8, a), acc, FMT,
+                                                        FMT, OPSEL, (int)sb, OPSEL, (int)sa);
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.  Used where
@@ -738,8 +773,18 @@ __device__ __forceinline__ void mx_stage(float* W, int lane, const float* v) {
 // Row r0 + l of the row copy gets columns c0 .. c0 + 31 (rows below rlim);
 // row c0 + l of the column copy gets token positions p0 .. p0 + 31 (when the
 // block starts inside the padded segment, p0 < pend).
+// (Element format F: E4M3 blocks take 32 code bytes, E2M1 blocks 16.)
+template <class F>
+__device__ __forceinline__ void mx_store_block(uint8_t* dst, const uint32_t* w) {
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  d[0] = u32x4{w[0], w[1], w[2], w[3]};
+  if constexpr (F::WORDS == 8) d[1] = u32x4{w[4], w[5], w[6], w[7]};
+}
+
+template <class F = FmtE4M3>
 __device__ __forceinline__ void mx_emit(const float* W, int lane, const GemmArgs& p, int r0,
                                         int rlim, int c0, int p0, int pend) {
+  constexpr int B = F::BYTES;
   const int l = lane & 31;
   float v[32];
   uint32_t w8[8];
@@ -754,19 +799,15 @@ __device__ __forceinline__ void mx_emit(const float* W, int lane, const GemmArgs
         v[4 * q + 2] = t[2];
         v[4 * q + 3] = t[3];
       }
-      const uint32_t sc = mx_quant32(v, w8);
-      u32x4* d = reinterpret_cast<u32x4*>(p.mxr + (size_t)row * p.ld_mxr + c0);
-      d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
-      d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+      const uint32_t sc = mx_quant32<F>(v, w8);
+      mx_store_block<F>(p.mxr + (size_t)row * (p.ld_mxr / 32 * B) + c0 / 32 * B, w8);
       p.mxr_s[(size_t)row * (p.ld_mxr / 32) + c0 / 32] = (uint8_t)sc;
     }
   } else if (p.mxc && p0 < pend) {
 #pragma unroll
     for (int r = 0; r < 32; ++r) v[r] = W[r * 36 + l];
-    const uint32_t sc = mx_quant32(v, w8);
-    u32x4* d = reinterpret_cast<u32x4*>(p.mxc + (size_t)(c0 + l) * p.ld_mxc + p0);
-    d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
-    d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+    const uint32_t sc = mx_quant32<F>(v, w8);
+    mx_store_block<F>(p.mxc + (size_t)(c0 + l) * (p.ld_mxc / 32 * B) + p0 / 32 * B, w8);
     p.mxc_s[(size_t)(c0 + l) * (p.ld_mxc / 32) + p0 / 32] = (uint8_t)sc;
   }
 }
@@ -901,19 +942,23 @@ struct GemmCfg {
   static constexpr int BKB = TL::BKB;
   static constexpr int BK = BKB / sizeof(typename EL::storage);   // k per pipeline step
   static constexpr bool MX = is_mx<EL>();
-  static constexpr int SUB = MX ? BKB / 64 : BKB / 32;             // MFMA k sub-steps per step
+  static constexpr int EPB = epb<EL>();                            // k elements per byte
+  static constexpr int SUB = MX ? BKB * EPB / 64 : BKB / 32;       // MFMA k sub-steps per step
   static constexpr int STAGES = TL::STAGES;                        // LDS ring depth
   // 16-byte units per stage: the A and B tiles, then (MX) one scale word per row
   static constexpr int STAGE_U4 = (BM + BN) * (BKB / 16) + (MX ? (BM + BN) / 4 : 0);
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_U4 * 16;
-  // MX epilogues stage 32 x 36 floats per wave in a free ring slot
+  // MX epilogues stage 32 x 36 floats per wave in the ring slots that are
+  // free after the main loop: STAGE_WAVES waves per slot, MX_SLOTS slots
   static constexpr int MX_STAGE_FLOATS = 32 * 36;
+  static constexpr int STAGE_WAVES = STAGE_U4 * 16 / (MX_STAGE_FLOATS * 4);
+  static constexpr int MX_SLOTS = (THREADS / 64 + STAGE_WAVES - 1) / STAGE_WAVES;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!epi_glu_fwd(EPI) || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
   static_assert(LDS_BYTES + 8320 <= 160 * 1024, "LDS ring does not fit");
-  static_assert(!MX || (THREADS / 64) * MX_STAGE_FLOATS * 4 <= STAGE_U4 * 16,
-                "MX epilogue staging must fit in one ring slot");
-  static_assert(!MX || BKB == 128, "MX steps are 128 k (four scale blocks, one word)");
+  static_assert(!MX || (STAGE_WAVES >= 1 && MX_SLOTS <= STAGES - 1),
+                "MX epilogue staging must fit in the free ring slots");
+  static_assert(!MX || BKB * EPB == 128, "MX steps are 128 k (four scale blocks, one word)");
 };
 
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false>
@@ -935,7 +980,9 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
   // ---- tile table (device-side shapes) ----
   for (int e = tid; e <= E; e += THREADS) {
     int o = p.offsets[e];
-    s_off[e] = o < 0 ? 0 : (o > p.R ? p.R : o);
+    o = o < 0 ? 0 : (o > p.R ? p.R : o);
+    // K counts bytes: MXFP4 weight-gradient segments (32-element aligned) halve
+    s_off[e] = GROUP == RAGGED_K ? o / epb<EL>() : o;
   }
   __syncthreads();
   int total;
@@ -1093,7 +1140,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       if (st < nk) {
         la.issue(stage_ptr(st), t.kb0 + st * BK);
         lb.issue(stage_ptr(st) + BM * CPR, t.kb0 + st * BK);
-        if constexpr (MX) ls.issue(scales_of(stage_ptr(st)), t.kb0 + st * BK);
+        if constexpr (MX) ls.issue(scales_of(stage_ptr(st)), (t.kb0 + st * BK) * C::EPB);
       }
   };
 
@@ -1201,7 +1248,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         u32x4* nb = stage_ptr(kt + S_ - 1);
         la.issue(nb, cur.kb0 + (kt + S_ - 1) * BK);
         lb.issue(nb + BM * CPR, cur.kb0 + (kt + S_ - 1) * BK);
-        if constexpr (MX) ls.issue(scales_of(nb), cur.kb0 + (kt + S_ - 1) * BK);
+        if constexpr (MX) ls.issue(scales_of(nb), (cur.kb0 + (kt + S_ - 1) * BK) * C::EPB);
       }
       const u32x4* As = stage_ptr(kt);
       const u32x4* Bs = As + BM * CPR;
@@ -1219,12 +1266,12 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         if constexpr (GROUP == RAGGED_K) {
           // blocks outside the segment read zero codes; their scale bytes
           // belong to other segments (or were never written): make them 1.0
-          const int b0 = (cur.kb0 + kt * BK) / 32 + h;
+          const int b0 = (cur.kb0 + kt * BK) * C::EPB / 32 + h;
           uint32_t keep = 0xffffffffu, fill = 0u;
 #pragma unroll
           for (int s2 = 0; s2 < SUB; ++s2) {
             const int b = b0 + 2 * s2;
-            if (b * 32 < cur.kbeg || b * 32 >= cur.kend) {
+            if (b * 32 < cur.kbeg * C::EPB || b * 32 >= cur.kend * C::EPB) {
               keep &= ~(0xffu << (16 * s2));
               fill |= 127u << (16 * s2);
             }
@@ -1236,13 +1283,13 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         }
         u32x8 af[2][TM], bfr[2][TN];
         auto frags = [&](int buf, int s2) {
-          af[buf][0] = FragMX<BM, BKB>::load(As, wm * C::WTM, s2, lane);
+          af[buf][0] = FragMX<BM, BKB, EL>::load(As, wm * C::WTM, s2, lane);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            bfr[buf][j] = FragMX<BN, BKB>::load(Bs, wn * C::WTN + 32 * j, s2, lane);
+            bfr[buf][j] = FragMX<BN, BKB, EL>::load(Bs, wn * C::WTN + 32 * j, s2, lane);
 #pragma unroll
           for (int i = 1; i < TM; ++i)
-            af[buf][i] = FragMX<BM, BKB>::load(As, wm * C::WTM + 32 * i, s2, lane);
+            af[buf][i] = FragMX<BM, BKB, EL>::load(As, wm * C::WTM + 32 * i, s2, lane);
         };
         frags(0, 0);
         static_for<0, SUB>([&](auto sc) {
@@ -1252,12 +1299,13 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
             constexpr int i = decltype(ic)::value;
             static_for<0, TN>([&](auto jc) {
               constexpr int j = decltype(jc)::value;
-              mma_mx<2 * s2>(acc[i][j], bfr[s2 & 1][j], af[s2 & 1][i], swb[j], swa[i]);
+              mma_mx<2 * s2, EL::FMT>(acc[i][j], bfr[s2 & 1][j], af[s2 & 1][i], swb[j],
+                                      swa[i]);
             });
           });
         });
         if constexpr (TL::SCHED == 1) {
-          constexpr int NR = (TM + TN) * FragMX<BM, BKB>::READS;
+          constexpr int NR = (TM + TN) * FragMX<BM, BKB, EL>::READS;
           constexpr int NM = TM * TN;
           __builtin_amdgcn_sched_group_barrier(0x100, NR + TM + TN, 0);
           static_for<0, SUB>([&](auto s2) {
@@ -1315,7 +1363,8 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       // zero in the column copy and skipped in the row copy.  The ring slot
       // after the last step's is free: its last reader passed the barrier of
       // the last step, and the next tile's loads start after a barrier.
-      float* Wt = reinterpret_cast<float*>(stage_ptr(nk)) + wave * C::MX_STAGE_FLOATS;
+      float* Wt = reinterpret_cast<float*>(stage_ptr(nk + wave / C::STAGE_WAVES)) +
+                  (wave % C::STAGE_WAVES) * C::MX_STAGE_FLOATS;
       const int pe0 = p.pad_offsets ? p.pad_offsets[e] : 0;
       const int pe1 = p.pad_offsets ? p.pad_offsets[e + 1] : 0;
       const int off_e = s_off[e];
@@ -1339,7 +1388,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                     p.gelu_tanh, rok, o);
                 mx_stage(Wt, lane, o);
                 wave_lds_sync();
-                mx_emit(Wt, lane, p, r0, mlim, (cb >> 6) * 32, prow, pe1);
+                mx_emit<typename EL::Fmt>(Wt, lane, p, r0, mlim, (cb >> 6) * 32, prow, pe1);
                 wave_lds_sync();
               }
             }
@@ -1352,11 +1401,11 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
               const int pg0 = (cb >> 5) * 64;
               mx_stage(Wt, lane, dg);
               wave_lds_sync();
-              mx_emit(Wt, lane, p, r0, mlim, pg0, prow, pe1);
+              mx_emit<typename EL::Fmt>(Wt, lane, p, r0, mlim, pg0, prow, pe1);
               wave_lds_sync();
               mx_stage(Wt, lane, dl);
               wave_lds_sync();
-              mx_emit(Wt, lane, p, r0, mlim, pg0 + 32, prow, pe1);
+              mx_emit<typename EL::Fmt>(Wt, lane, p, r0, mlim, pg0 + 32, prow, pe1);
               wave_lds_sync();
             }
           }
@@ -1524,9 +1573,16 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
 // 4 waves at 128 x 128 for small problems.
 typedef Tile<256, 256, 2, 4, 128, 2, 1> TMxBig;
 typedef Tile<128, 128, 2, 2, 128, 2> TMxSmall;
+// MXFP4: 64-byte steps (128 k, one scale word) in a three-deep ring.
+typedef Tile<256, 256, 2, 4, 64, 3, 1> TMx4Big;
+typedef Tile<128, 128, 2, 2, 64, 3> TMx4Small;
 
 template <int GROUP, int EPI>
-moe_status_t dispatch_mx(const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
+moe_status_t dispatch_mx(const GemmArgs& p, bool big, int max_cus, hipStream_t s, int dtype) {
+  if (dtype == MOE_E2M1) {
+    if (big) return launch_gemm<MX4, true, true, GROUP, EPI, TMx4Big>(p, max_cus, s);
+    return launch_gemm<MX4, true, true, GROUP, EPI, TMx4Small>(p, max_cus, s);
+  }
   if (big) return launch_gemm<MX8, true, true, GROUP, EPI, TMxBig>(p, max_cus, s);
   return launch_gemm<MX8, true, true, GROUP, EPI, TMxSmall>(p, max_cus, s);
 }
@@ -1598,18 +1654,24 @@ inline bool mx_in_ok(const moe_mx_t* m, long long K) {
 inline bool mx_out_ok(const moe_mx_t* m, long long n) {
   return m && m->data && m->scale && m->ld >= n && m->ld % 32 == 0 && aligned16(m->data);
 }
-inline void set_mx_a(GemmArgs& p, const moe_mx_t* m) {
+// Bytes per code row: E4M3 one per element, E2M1 two elements per byte.
+inline long long mx_row_bytes(const moe_mx_t* m, int dtype) {
+  return dtype == MOE_E2M1 ? m->ld / 2 : m->ld;
+}
+inline int mx_epb(int dtype) { return dtype == MOE_E2M1 ? 2 : 1; }
+
+inline void set_mx_a(GemmArgs& p, const moe_mx_t* m, int dtype) {
   p.a = m->data;
-  p.lda = m->ld;
+  p.lda = mx_row_bytes(m, dtype);
   p.sa = m->scale;
   p.slda = m->ld / 32;
 }
-inline void set_mx_b(GemmArgs& p, const moe_mx_t* m, long long rows_per_expert) {
+inline void set_mx_b(GemmArgs& p, const moe_mx_t* m, long long rows_per_expert, int dtype) {
   p.b = m->data;
-  p.ldb = m->ld;
+  p.ldb = mx_row_bytes(m, dtype);
   p.sb = m->scale;
   p.sldb = m->ld / 32;
-  p.b_expert_stride = rows_per_expert * m->ld;
+  p.b_expert_stride = rows_per_expert * p.ldb;
   p.sb_expert_stride = rows_per_expert * (m->ld / 32);
 }
 inline void set_mx_out(GemmArgs& p, moe_mx_t* row, moe_mx_t* col, const int32_t* pad) {
@@ -1628,6 +1690,7 @@ inline void set_mx_out(GemmArgs& p, moe_mx_t* row, moe_mx_t* col, const int32_t*
 
 // MXFP8 FC1 + GLU (dtype == MOE_E4M3).
 moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
+  const int dt = a->dtype;
   MOE_CHECK_ARG(a->struct_size >= offsetof(moe_glu_fwd_args_t, src_row));
   MOE_CHECK_ARG(!gather_field(a, &moe_glu_fwd_args_t::src_row));
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU);
@@ -1639,13 +1702,13 @@ moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
   MOE_CHECK_ARG(!a->a_col || (mx_out_ok(a->a_col, moe_mx_col_len(a->R, a->E)) && a->pad_offsets));
   MOE_CHECK_ARG(aligned16(a->h_out));
   GemmArgs p = zero_args();
-  set_mx_a(p, a->xp_mx);
-  set_mx_b(p, a->w1_mx, n1);
+  set_mx_a(p, a->xp_mx, dt);
+  set_mx_b(p, a->w1_mx, n1, dt);
   p.offsets = a->offsets;
   p.E = a->E;
   p.R = a->R;
   p.N = n1;
-  p.K = a->d;
+  p.K = a->d / mx_epb(dt);
   p.aux = a->h_out;
   p.ld_aux = n1;
   set_mx_out(p, a->a_row, a->a_col, a->pad_offsets);
@@ -1654,30 +1717,33 @@ moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
   p.act = a->act;
   p.gelu_tanh = a->gelu_tanh;
   const bool big = big_ragged_m(a->R, a->E, n1);
-  if (a->act == MOE_ACT_SWIGLU) return dispatch_mx<RAGGED_M, EPI_SWIGLU_FWD>(p, big, a->max_cus, s);
-  return dispatch_mx<RAGGED_M, EPI_GEGLU_FWD>(p, big, a->max_cus, s);
+  if (a->act == MOE_ACT_SWIGLU)
+    return dispatch_mx<RAGGED_M, EPI_SWIGLU_FWD>(p, big, a->max_cus, s, dt);
+  return dispatch_mx<RAGGED_M, EPI_GEGLU_FWD>(p, big, a->max_cus, s, dt);
 }
 
 moe_status_t gemm_fwd_mx(const moe_gemm_fwd_args_t* a, hipStream_t s) {
+  const int dt = a->dtype;
   MOE_CHECK_ARG(a->struct_size >= sizeof(moe_gemm_fwd_args_t));
   MOE_CHECK_ARG(a->b == nullptr && a->K % 128 == 0);
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->offsets && a->y && aligned16(a->y));
   MOE_CHECK_ARG(mx_in_ok(a->a_mx, a->K) && mx_in_ok(a->w_mx, a->K));
   GemmArgs p = zero_args();
-  set_mx_a(p, a->a_mx);
-  set_mx_b(p, a->w_mx, a->N);
+  set_mx_a(p, a->a_mx, dt);
+  set_mx_b(p, a->w_mx, a->N, dt);
   p.offsets = a->offsets;
   p.E = a->E;
   p.R = a->R;
   p.N = a->N;
-  p.K = a->K;
+  p.K = a->K / mx_epb(dt);
   p.c = a->y;
   p.ldc = a->N;
-  return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->N), a->max_cus, s);
+  return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->N), a->max_cus, s, dt);
 }
 
 moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
+  const int dt = a->dtype;
   MOE_CHECK_ARG(a->struct_size >= sizeof(moe_glu_bwd_args_t));
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU);
   MOE_CHECK_ARG(a->d % 128 == 0);
@@ -1689,13 +1755,13 @@ moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
   MOE_CHECK_ARG(!a->dh_col ||
                 (mx_out_ok(a->dh_col, moe_mx_col_len(a->R, a->E)) && a->pad_offsets));
   GemmArgs p = zero_args();
-  set_mx_a(p, a->dy_mx);
-  set_mx_b(p, a->w2t_mx, a->f);
+  set_mx_a(p, a->dy_mx, dt);
+  set_mx_b(p, a->w2t_mx, a->f, dt);
   p.offsets = a->offsets;
   p.E = a->E;
   p.R = a->R;
   p.N = a->f;
-  p.K = a->d;
+  p.K = a->d / mx_epb(dt);
   p.aux = const_cast<void*>(a->h);
   p.ld_aux = n1;
   set_mx_out(p, a->dh_row, a->dh_col, a->pad_offsets);
@@ -1704,11 +1770,13 @@ moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
   p.act = a->act;
   p.gelu_tanh = a->gelu_tanh;
   const bool big = big_ragged_m(a->R, a->E, a->f);
-  if (a->act == MOE_ACT_SWIGLU) return dispatch_mx<RAGGED_M, EPI_SWIGLU_BWD>(p, big, a->max_cus, s);
-  return dispatch_mx<RAGGED_M, EPI_GEGLU_BWD>(p, big, a->max_cus, s);
+  if (a->act == MOE_ACT_SWIGLU)
+    return dispatch_mx<RAGGED_M, EPI_SWIGLU_BWD>(p, big, a->max_cus, s, dt);
+  return dispatch_mx<RAGGED_M, EPI_GEGLU_BWD>(p, big, a->max_cus, s, dt);
 }
 
 moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
+  const int dt = a->dtype;
   MOE_CHECK_ARG(a->struct_size >= offsetof(moe_gemm_bwd_args_t, a_src_row));
   MOE_CHECK_ARG(!gather_field(a, &moe_gemm_bwd_args_t::a_src_row));
   GemmArgs p = zero_args();
@@ -1718,15 +1786,16 @@ moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
     MOE_CHECK_ARG(a->N % 128 == 0);
     if (a->R == 0) return MOE_OK;
     MOE_CHECK_ARG(a->offsets && mx_in_ok(a->g_mx, a->N) && mx_in_ok(a->w_mx, a->N));
-    set_mx_a(p, a->g_mx);
-    set_mx_b(p, a->w_mx, a->K);
+    set_mx_a(p, a->g_mx, dt);
+    set_mx_b(p, a->w_mx, a->K, dt);
     p.offsets = a->offsets;
     p.R = a->R;
     p.N = a->K;
-    p.K = a->N;
+    p.K = a->N / mx_epb(dt);
     p.c = a->out;
     p.ldc = a->K;
-    return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->K), a->max_cus, s);
+    return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->K), a->max_cus, s,
+                                            dt);
   }
   // dw[e] [N, K] = g_col[:, seg e] @ a_col[:, seg e]^T; the k ranges are the
   // padded segments, so the offsets table is pad_offsets and R its bound
@@ -1734,8 +1803,8 @@ moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
   const long long L = moe_mx_col_len(a->R, a->E);
   MOE_CHECK_ARG(mx_in_ok(a->g_mx, L) && mx_in_ok(a->a_mx, L));
   MOE_CHECK_ARG(L <= 0x7fffffff);
-  set_mx_a(p, a->g_mx);
-  set_mx_b(p, a->a_mx, 0);
+  set_mx_a(p, a->g_mx, dt);
+  set_mx_b(p, a->a_mx, 0, dt);
   p.offsets = a->pad_offsets;
   p.R = (int)L;
   p.M = a->N;
@@ -1745,18 +1814,19 @@ moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
   p.c_expert_stride = (long long)a->N * a->K;
   p.accumulate = a->accumulate;
   return dispatch_mx<RAGGED_K, EPI_STORE>(p, big_ragged_k(a->R, a->E, a->N, a->K), a->max_cus,
-                                          s);
+                                          s, dt);
 }
 
 extern "C" {
 
 moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream) {
   MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_glu_fwd_args_t, xp_mx));
-  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1 || valid_dtype(a->dtype));
   MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->d > 0 && a->f > 0 && a->d % 32 == 0 && a->f % 32 == 0);
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU || a->act == MOE_ACT_SRELU);
-  if (a->dtype == MOE_E4M3) return glu_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
+    return glu_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->xp && a->w1p && a->offsets && a->a_out);
   MOE_CHECK_ARG(aligned16(a->xp) && aligned16(a->w1p) && aligned16(a->a_out) &&
@@ -1800,10 +1870,11 @@ moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream)
 
 moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* a, void* stream) {
   MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_gemm_fwd_args_t, a_mx));
-  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1 || valid_dtype(a->dtype));
   MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->N > 0 && a->K > 0 && a->N % 8 == 0 && a->K % 8 == 0);
-  if (a->dtype == MOE_E4M3) return gemm_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
+    return gemm_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->a && a->w && a->offsets && a->y);
   MOE_CHECK_ARG(aligned16(a->a) && aligned16(a->w) && aligned16(a->y) && aligned16(a->b));
@@ -1829,11 +1900,12 @@ moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* a, void* stream) {
 
 moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream) {
   MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_glu_bwd_args_t, dy_mx));
-  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1 || valid_dtype(a->dtype));
   MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->d > 0 && a->f > 0 && a->d % 32 == 0 && a->f % 32 == 0);
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU || a->act == MOE_ACT_SRELU);
-  if (a->dtype == MOE_E4M3) return glu_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
+    return glu_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->dy && a->w2 && a->h && a->offsets && a->dh);
   MOE_CHECK_ARG(aligned16(a->dy) && aligned16(a->w2) && aligned16(a->h) && aligned16(a->dh));
@@ -1869,12 +1941,13 @@ moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream)
 
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
   MOE_CHECK_ARG(a && a->struct_size >= offsetof(moe_gemm_bwd_args_t, g_mx));
-  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || valid_dtype(a->dtype));
+  MOE_CHECK_ARG(a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1 || valid_dtype(a->dtype));
   MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->N > 0 && a->K > 0 && a->N % 8 == 0 && a->K % 8 == 0);
   MOE_CHECK_ARG(a->mode == MOE_BWD_DGRAD || a->mode == MOE_BWD_WGRAD);
   MOE_CHECK_ARG(a->out && aligned16(a->out));
-  if (a->dtype == MOE_E4M3) return gemm_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
+    return gemm_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   MOE_CHECK_ARG(a->g && a->offsets && aligned16(a->g));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   GemmArgs p = zero_args();

@@ -1,5 +1,7 @@
-// MXFP8 quantizers (E4M3 elements, one E8M0 scale per 32): row copies,
-// transposed weight copies and expert-segmented column copies.
+// MXFP8 / MXFP4 quantizers (E4M3 or E2M1 elements, one E8M0 scale per 32):
+// row copies, transposed weight copies and expert-segmented column copies.
+// Code rows hold F::BYTES bytes per 32 elements (ld elements = ld * BYTES / 32
+// bytes).
 //
 // [P1] "高度な融合カーネルによる MoE 学習スループットの向上", section
 // "MXFP8 および NVFP4 量子化の融合による露出メモリオーバーヘッドの削減": GEMM
@@ -28,9 +30,17 @@ __device__ __forceinline__ float row_gate(const int32_t* __restrict__ row_map,
   return w;
 }
 
+// The F::BYTES code bytes of one block (16-byte aligned).
+template <class F>
+__device__ __forceinline__ void store_block(uint8_t* dst, const uint32_t* w) {
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  d[0] = u32x4{w[0], w[1], w[2], w[3]};
+  if constexpr (F::WORDS == 8) d[1] = u32x4{w[4], w[5], w[6], w[7]};
+}
+
 // Row copy: eight lanes per 32-block, four values per lane; a wave covers
 // eight consecutive blocks (512 contiguous bytes of bf16 input).
-template <class EL>
+template <class EL, class F>
 __global__ void __launch_bounds__(256)
     mx_rows_kernel(const typename EL::storage* __restrict__ x, long long rows, int n,
                    const int32_t* __restrict__ src_row, const int32_t* __restrict__ row_map,
@@ -57,12 +67,20 @@ __global__ void __launch_bounds__(256)
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-    const int e = mx_exponent(amax);
+    const int e = mx_exponent<F::EMAX>(amax);
     const float inv = mx_inv_scale(e);
-    uint32_t word = 0;
+    const long long ldb = ld / 32 * F::BYTES;
+    if constexpr (F::WORDS == 8) {
+      uint32_t word = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) word |= e4m3_code(v[q] * inv) << (8 * q);
-    *reinterpret_cast<uint32_t*>(codes + r * ld + 32 * b + 4 * sub) = word;
+      for (int q = 0; q < 4; ++q) word |= e4m3_code(v[q] * inv) << (8 * q);
+      *reinterpret_cast<uint32_t*>(codes + r * ldb + 32 * b + 4 * sub) = word;
+    } else {
+      uint32_t half = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) half |= e2m1_code(v[q] * inv) << (4 * q);
+      *reinterpret_cast<uint16_t*>(codes + r * ldb + 16 * b + 2 * sub) = (uint16_t)half;
+    }
     if (sub == 0) scales[r * (ld / 32) + b] = (uint8_t)(e + 127);
   }
 }
@@ -71,7 +89,7 @@ __global__ void __launch_bounds__(256)
 // 32 rows for 256 columns, thread c holding column c (its 32 values come from
 // 32 coalesced row reads of the workgroup) and writing 32 contiguous code
 // bytes of output row b n + c.  (Weights only: made once, outside the layer.)
-template <class EL>
+template <class EL, class F>
 __global__ void __launch_bounds__(256)
     mx_transpose_kernel(const typename EL::storage* __restrict__ x, int n, int rows,
                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, long long ld,
@@ -86,10 +104,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = ld1(x + (b * rows + prow0 + i) * n + c);
       uint32_t w[8];
-      const uint32_t sc = mx_quant32(v, w);
-      u32x4* dst = reinterpret_cast<u32x4*>(codes + (b * n + c) * ld + prow0);
-      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+      const uint32_t sc = mx_quant32<F>(v, w);
+      store_block<F>(codes + (b * n + c) * (ld / 32 * F::BYTES) + prow0 / 32 * F::BYTES, w);
       scales[(b * n + c) * (ld / 32) + prow0 / 32] = (uint8_t)sc;
     }
   }
@@ -103,7 +119,7 @@ __global__ void __launch_bounds__(256)
 // the 32 rows into the column copy (consecutive columns: distinct banks).
 constexpr int TILE_LD = 260;
 
-template <class EL>
+template <class EL, class F>
 __global__ void __launch_bounds__(256)
     mx_rowcol_kernel(const typename EL::storage* __restrict__ x, int n, int E,
                      const int32_t* __restrict__ offsets, const int32_t* __restrict__ pad_offsets,
@@ -175,10 +191,8 @@ __global__ void __launch_bounds__(256)
           v[4 * q + 2] = t[2];
           v[4 * q + 3] = t[3];
         }
-        const uint32_t sc = mx_quant32(v, w8);
-        u32x4* d = reinterpret_cast<u32x4*>(rcodes + (size_t)r * rld + col);
-        d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
-        d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+        const uint32_t sc = mx_quant32<F>(v, w8);
+        store_block<F>(rcodes + (size_t)r * (rld / 32 * F::BYTES) + col / 32 * F::BYTES, w8);
         rscales[(size_t)r * (rld / 32) + col / 32] = (uint8_t)sc;
       }
     }
@@ -186,10 +200,9 @@ __global__ void __launch_bounds__(256)
     if (ccodes && c0 + tid < n) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = tile[i * TILE_LD + tid];
-      const uint32_t sc = mx_quant32(v, w8);
-      u32x4* d = reinterpret_cast<u32x4*>(ccodes + (size_t)(c0 + tid) * cld + prow0);
-      d[0] = u32x4{w8[0], w8[1], w8[2], w8[3]};
-      d[1] = u32x4{w8[4], w8[5], w8[6], w8[7]};
+      const uint32_t sc = mx_quant32<F>(v, w8);
+      store_block<F>(ccodes + (size_t)(c0 + tid) * (cld / 32 * F::BYTES) + prow0 / 32 * F::BYTES,
+                     w8);
       cscales[(size_t)(c0 + tid) * (cld / 32) + prow0 / 32] = (uint8_t)sc;
     }
     __syncthreads();
@@ -206,34 +219,34 @@ int grid_for(long long work, int per_block, int cap) {
   return (int)(g > cap ? cap : g);
 }
 
-template <class EL>
+template <class EL, class F>
 void launch_rows(const void* x, long long rows, int n, const int32_t* src_row,
                  const int32_t* row_map, const float* topk_w, int k, const moe_mx_t* out,
                  hipStream_t s) {
   const long long blocks = rows * (n / 32);
-  hipLaunchKernelGGL(mx_rows_kernel<EL>, dim3(grid_for(blocks, 32, 16384)), dim3(256), 0, s,
+  hipLaunchKernelGGL((mx_rows_kernel<EL, F>), dim3(grid_for(blocks, 32, 16384)), dim3(256), 0, s,
                      reinterpret_cast<const typename EL::storage*>(x), rows, n, src_row, row_map,
                      topk_w, k, out->data, out->scale, (long long)out->ld);
 }
 
-template <class EL>
+template <class EL, class F>
 void launch_transpose(const void* x, int n, int rows, const moe_mx_t* out, long long ngroups,
                       hipStream_t s) {
   const int gx = (n + 255) / 256;
   const int gy = (int)(ngroups > 16384 ? 16384 : ngroups);
-  hipLaunchKernelGGL(mx_transpose_kernel<EL>, dim3(gx, gy), dim3(256), 0, s,
+  hipLaunchKernelGGL((mx_transpose_kernel<EL, F>), dim3(gx, gy), dim3(256), 0, s,
                      reinterpret_cast<const typename EL::storage*>(x), n, rows, out->data,
                      out->scale, (long long)out->ld, ngroups);
 }
 
-template <class EL>
+template <class EL, class F>
 void launch_rowcol(const void* x, int n, int E, const int32_t* offsets, const int32_t* pad_offsets,
                    const int32_t* src_row, const int32_t* row_map, const float* topk_w, int k,
                    const moe_mx_t* row_out, const moe_mx_t* col_out, long long ngroups,
                    hipStream_t s) {
   const int gx = (n + 255) / 256;
   const int gy = (int)(ngroups > 16384 ? 16384 : ngroups);
-  hipLaunchKernelGGL(mx_rowcol_kernel<EL>, dim3(gx, gy), dim3(256), 0, s,
+  hipLaunchKernelGGL((mx_rowcol_kernel<EL, F>), dim3(gx, gy), dim3(256), 0, s,
                      reinterpret_cast<const typename EL::storage*>(x), n, E, offsets, pad_offsets,
                      src_row, row_map, topk_w, k, row_out ? row_out->data : nullptr,
                      row_out ? row_out->scale : nullptr, row_out ? (long long)row_out->ld : 0LL,
@@ -242,30 +255,21 @@ void launch_rowcol(const void* x, int n, int E, const int32_t* offsets, const in
 
 }  // namespace
 
-}  // namespace moe
-
-using namespace moe;
-
-extern "C" {
-
-int64_t moe_mx_col_len(int R, int E) {
-  const int64_t n = (int64_t)R + 31 * (int64_t)E;
-  return (n + 127) / 128 * 128;
-}
-
-moe_status_t moe_mx_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
+template <class F>
+moe_status_t mx_quantize_impl(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
                              void* stream) {
   MOE_CHECK_ARG(valid_dtype(dtype) && rows >= 0 && n > 0 && n % 32 == 0);
   MOE_CHECK_ARG(mx_ok(out) && out->ld >= n);
   MOE_CHECK_ARG(rows == 0 || (x && aligned16(x)));
   if (rows == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == MOE_BF16) launch_rows<BF16>(x, rows, n, nullptr, nullptr, nullptr, 0, out, s);
-  else launch_rows<F32>(x, rows, n, nullptr, nullptr, nullptr, 0, out, s);
+  if (dtype == MOE_BF16) launch_rows<BF16, F>(x, rows, n, nullptr, nullptr, nullptr, 0, out, s);
+  else launch_rows<F32, F>(x, rows, n, nullptr, nullptr, nullptr, 0, out, s);
   return launch_status();
 }
 
-moe_status_t moe_mx_quantize_transpose(const void* x, int dtype, int batches, int rows, int n,
+template <class F>
+moe_status_t mx_quantize_transpose_impl(const void* x, int dtype, int batches, int rows, int n,
                                        moe_mx_t* out, void* stream) {
   MOE_CHECK_ARG(valid_dtype(dtype) && batches >= 0 && rows >= 0 && rows % 32 == 0 && n > 0);
   MOE_CHECK_ARG(mx_ok(out) && out->ld >= rows);
@@ -273,12 +277,13 @@ moe_status_t moe_mx_quantize_transpose(const void* x, int dtype, int batches, in
   MOE_CHECK_ARG(groups == 0 || (x && aligned16(x)));
   if (groups == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == MOE_BF16) launch_transpose<BF16>(x, n, rows, out, groups, s);
-  else launch_transpose<F32>(x, n, rows, out, groups, s);
+  if (dtype == MOE_BF16) launch_transpose<BF16, F>(x, n, rows, out, groups, s);
+  else launch_transpose<F32, F>(x, n, rows, out, groups, s);
   return launch_status();
 }
 
-moe_status_t moe_mx_quantize_experts(const void* x, int dtype, const int32_t* src_row,
+template <class F>
+moe_status_t mx_quantize_experts_impl(const void* x, int dtype, const int32_t* src_row,
                                      const int32_t* row_map, const float* topk_w, int k,
                                      const int32_t* offsets, const int32_t* pad_offsets, int E,
                                      int R, int n, moe_mx_t* row_out, moe_mx_t* col_out,
@@ -299,17 +304,61 @@ moe_status_t moe_mx_quantize_experts(const void* x, int dtype, const int32_t* sr
     // both copies from one read of the rows
     const long long groups = moe_mx_col_len(R, E) / 32;
     if (bf)
-      launch_rowcol<BF16>(x, n, E, offsets, pad_offsets, src_row, row_map, topk_w, k, row_out,
-                          col_out, groups, s);
+      launch_rowcol<BF16, F>(x, n, E, offsets, pad_offsets, src_row, row_map, topk_w, k, row_out,
+                             col_out, groups, s);
     else
-      launch_rowcol<F32>(x, n, E, offsets, pad_offsets, src_row, row_map, topk_w, k, row_out,
-                         col_out, groups, s);
+      launch_rowcol<F32, F>(x, n, E, offsets, pad_offsets, src_row, row_map, topk_w, k, row_out,
+                            col_out, groups, s);
   } else if (bf) {
-    launch_rows<BF16>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
+    launch_rows<BF16, F>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
   } else {
-    launch_rows<F32>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
+    launch_rows<F32, F>(x, R, n, src_row, row_map, topk_w, k, row_out, s);
   }
   return launch_status();
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int64_t moe_mx_col_len(int R, int E) {
+  const int64_t n = (int64_t)R + 31 * (int64_t)E;
+  return (n + 127) / 128 * 128;
+}
+
+moe_status_t moe_mx_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
+                             void* stream) {
+  return mx_quantize_impl<FmtE4M3>(x, dtype, rows, n, out, stream);
+}
+moe_status_t moe_mxfp4_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
+                                void* stream) {
+  return mx_quantize_impl<FmtE2M1>(x, dtype, rows, n, out, stream);
+}
+moe_status_t moe_mx_quantize_transpose(const void* x, int dtype, int batches, int rows, int n,
+                                       moe_mx_t* out, void* stream) {
+  return mx_quantize_transpose_impl<FmtE4M3>(x, dtype, batches, rows, n, out, stream);
+}
+moe_status_t moe_mxfp4_quantize_transpose(const void* x, int dtype, int batches, int rows, int n,
+                                          moe_mx_t* out, void* stream) {
+  return mx_quantize_transpose_impl<FmtE2M1>(x, dtype, batches, rows, n, out, stream);
+}
+moe_status_t moe_mx_quantize_experts(const void* x, int dtype, const int32_t* src_row,
+                                     const int32_t* row_map, const float* topk_w, int k,
+                                     const int32_t* offsets, const int32_t* pad_offsets, int E,
+                                     int R, int n, moe_mx_t* row_out, moe_mx_t* col_out,
+                                     void* stream) {
+  return mx_quantize_experts_impl<FmtE4M3>(x, dtype, src_row, row_map, topk_w, k, offsets,
+                                           pad_offsets, E, R, n, row_out, col_out, stream);
+}
+moe_status_t moe_mxfp4_quantize_experts(const void* x, int dtype, const int32_t* src_row,
+                                        const int32_t* row_map, const float* topk_w, int k,
+                                        const int32_t* offsets, const int32_t* pad_offsets, int E,
+                                        int R, int n, moe_mx_t* row_out, moe_mx_t* col_out,
+                                        void* stream) {
+  return mx_quantize_experts_impl<FmtE2M1>(x, dtype, src_row, row_map, topk_w, k, offsets,
+                                           pad_offsets, E, R, n, row_out, col_out, stream);
 }
 
 }  // extern "C"

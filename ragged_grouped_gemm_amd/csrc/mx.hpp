@@ -13,6 +13,11 @@
 //     e = floor(log2 amax) - 8 (8 = exponent of E4M3's largest normal),
 //     clamped to [-127, 127], and e = -127 for amax = 0; each value is
 //     v / 2^e rounded to nearest even E4M3, saturated to +-448.
+// MXFP4 (same specification) uses E2M1 elements: sign, 2 exponent bits (bias
+// 1), 1 mantissa bit, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, no NaN; the block
+// exponent is floor(log2 amax) - 2 (2 = exponent of 6); codes are packed two
+// per byte, element 2 i in the low nibble of byte i; a NaN input becomes the
+// largest magnitude with its sign.
 // Everything below is exact integer / power-of-two arithmetic on float32.
 #pragma once
 
@@ -20,16 +25,18 @@
 
 namespace moe {
 
-// Shared exponent of a block from its largest magnitude (finite, >= 0).
+// Shared exponent of a block from its largest magnitude (finite, >= 0);
+// EMAX is the exponent of the element format's largest normal.
+template <int EMAX = 8>
 __device__ __forceinline__ int mx_exponent(float amax) {
   const uint32_t b = __float_as_uint(amax);
   const int ef = (int)(b >> 23) & 0xff;  // 0 for zero and float32 subnormals
   if (ef == 0) return -127;              // floor(log2 amax) <= -127 -> clamped
-  const int e = ef - 127 - 8;
+  const int e = ef - 127 - EMAX;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// 2^-e as a float32 (e in [-127, 119] for any finite float32 amax, so the
+// 2^-e as a float32 (e in [-127, 125] for any finite float32 amax, so the
 // result is a normal float32 and the scaling is exact).
 __device__ __forceinline__ float mx_inv_scale(int e) {
   return __uint_as_float((uint32_t)(127 - e) << 23);
@@ -55,20 +62,52 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | (r - ((127u - 7u) << 3));
 }
 
-// Quantize 32 values: returns the scale code, writes 8 little-endian words of
-// element codes (value i in byte i % 4 of word i / 4).
+// E2M1 code of a float32 value (already divided by the block scale): round
+// to nearest even, saturate at 6.  Each comparison adds one step; the ties
+// (0.25, 0.75, ...) fall to the neighbour with the even code.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 28) & 0x8u;
+  const float a = __uint_as_float(u & 0x7fffffffu);
+  if (a != a) return sign | 7u;
+  return sign | (uint32_t)((a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                           (a > 2.5f) + (a >= 3.5f) + (a > 5.0f));
+}
+
+// Element formats: exponent of the largest normal, code words per 32 values.
+struct FmtE4M3 {
+  static constexpr int EMAX = 8, WORDS = 8, BYTES = 32;
+};
+struct FmtE2M1 {
+  static constexpr int EMAX = 2, WORDS = 4, BYTES = 16;
+};
+
+// Quantize 32 values: returns the scale code, writes F::WORDS little-endian
+// words of element codes (E4M3: value i in byte i % 4 of word i / 4; E2M1:
+// value i in bits 4 (i % 8) .. of word i / 8).
+template <class F = FmtE4M3>
 __device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* w) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int e = mx_exponent(amax);
+  const int e = mx_exponent<F::EMAX>(amax);
   const float inv = mx_inv_scale(e);
+  if constexpr (F::WORDS == 8) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t x = 0;
+    for (int i = 0; i < 8; ++i) {
+      uint32_t x = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) x |= e4m3_code(v[4 * i + q] * inv) << (8 * q);
-    w[i] = x;
+      for (int q = 0; q < 4; ++q) x |= e4m3_code(v[4 * i + q] * inv) << (8 * q);
+      w[i] = x;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x |= e2m1_code(v[8 * i + q] * inv) << (4 * q);
+      w[i] = x;
+    }
   }
   return (uint32_t)(e + 127);
 }

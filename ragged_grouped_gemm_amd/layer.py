@@ -23,7 +23,8 @@ as usual.  Between the passes the layer then needs only the routing, Y and
 its inputs, at the price of one more FC1 GEMM (4·R·d·f FLOP) per backward;
 the gradients are bit-identical to the stored-H path.
 
-MXFP8 variant (``gemm="mxfp8"``): every GEMM operand is an MXFP8 copy blocked
+MXFP8 variant (``gemm="mxfp8"``; ``gemm="mxfp4"`` is the same with E2M1
+elements): every GEMM operand is an MXFP8 copy blocked
 along that GEMM's reduction axis.  Xp and dY exist only as MXFP8 row and
 expert-segmented column copies written straight from x and d_out; FC1's
 epilogue writes A, and the dGLU epilogue dH, as the same two copies; H stays
@@ -40,16 +41,18 @@ from . import ops
 
 
 class MXWeights:
-    """MXFP8 copies of the expert weights: W1p [E, 2f, d] blocked along d (FC1)
-    and along 2f (FC1 dgrad, stored transposed [E*d, 2f]); W2 [E, d, f] along f
-    (FC2) and along d (FC2 dgrad, stored transposed [E*f, d])."""
+    """MX copies (MXFP8, or MXFP4 with fmt="e2m1") of the expert weights: W1p
+    [E, 2f, d] blocked along d (FC1) and along 2f (FC1 dgrad, stored transposed
+    [E*d, 2f]); W2 [E, d, f] along f (FC2) and along d (FC2 dgrad, stored
+    transposed [E*f, d])."""
 
-    def __init__(self, W1p, W2):
+    def __init__(self, W1p, W2, fmt="e4m3"):
         E, n1, d = W1p.shape
-        self.w1 = ops.moe_mx_quantize(W1p.reshape(E * n1, d))
-        self.w1t = ops.moe_mx_quantize_transpose(W1p)
-        self.w2 = ops.moe_mx_quantize(W2.reshape(-1, W2.shape[2]))
-        self.w2t = ops.moe_mx_quantize_transpose(W2)
+        self.fmt = fmt
+        self.w1 = ops.moe_mx_quantize(W1p.reshape(E * n1, d), fmt=fmt)
+        self.w1t = ops.moe_mx_quantize_transpose(W1p, fmt=fmt)
+        self.w2 = ops.moe_mx_quantize(W2.reshape(-1, W2.shape[2]), fmt=fmt)
+        self.w2t = ops.moe_mx_quantize_transpose(W2, fmt=fmt)
 
 
 class MoEFFN:
@@ -58,7 +61,10 @@ class MoEFFN:
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
                  recompute=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
-        self.mx = gemm == "mxfp8"
+        if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
+            raise ValueError(gemm)
+        self.mx = gemm in ("mxfp8", "mxfp4")
+        self.mx_fmt = "e2m1" if gemm == "mxfp4" else "e4m3"
         if recompute and (self.mx or not backward):
             raise ValueError("recompute applies to the bf16 / fp32 training layer")
         self.recompute = recompute
@@ -113,8 +119,12 @@ class MoEFFN:
         L = ops.moe_mx_col_len(R, E)
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
 
+        fmt = self.mx_fmt
+        nb = (lambda ld: ld // 2) if fmt == "e2m1" else (lambda ld: ld)
+
         def mx(rows, ld):
-            return ops.MXTensor(rows, ld, dev, z((rows, ld), u8), z((rows, ld // 32), u8))
+            return ops.MXTensor(rows, ld, dev, z((rows, nb(ld)), u8), z((rows, ld // 32), u8),
+                                fmt=fmt)
 
         self.pad_offsets = z((E + 1,), torch.int32)
         self.xp_row, self.xp_col = mx(R, d), mx(d, L)
@@ -134,8 +144,8 @@ class MoEFFN:
             self.db1p = self.db2 = None
 
     @staticmethod
-    def mx_weights(W1p, W2):
-        return MXWeights(W1p, W2)
+    def mx_weights(W1p, W2, gemm="mxfp8"):
+        return MXWeights(W1p, W2, "e2m1" if gemm == "mxfp4" else "e4m3")
 
     # ------------------------------------------------------------------ passes
 

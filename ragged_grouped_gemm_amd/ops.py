@@ -43,16 +43,25 @@ def _empty(shape, dtype, like):
 
 
 class MXTensor:
-    """An MXFP8 matrix (moe_mx_t): E4M3 codes ``data`` [rows, ld] (uint8) and
-    E8M0 scales ``scale`` [rows, ld / 32] (uint8)."""
+    """An MX matrix (moe_mx_t): element codes ``data`` (uint8; E4M3 [rows, ld],
+    or E2M1 packed two per byte [rows, ld / 2] when ``fmt == "e2m1"``) and E8M0
+    scales ``scale`` [rows, ld / 32] (uint8)."""
 
-    def __init__(self, rows: int, ld: int, device, data=None, scale=None):
+    def __init__(self, rows: int, ld: int, device, data=None, scale=None, fmt: str = "e4m3"):
         if ld % 32:
             raise ValueError("ld must be a multiple of 32")
+        if fmt not in ("e4m3", "e2m1"):
+            raise ValueError(fmt)
         self.ld = ld
-        self.data = torch.empty((rows, ld), dtype=torch.uint8, device=device) if data is None else data
+        self.fmt = fmt
+        nb = ld if fmt == "e4m3" else ld // 2
+        self.data = torch.empty((rows, nb), dtype=torch.uint8, device=device) if data is None else data
         self.scale = (torch.empty((rows, ld // 32), dtype=torch.uint8, device=device)
                       if scale is None else scale)
+
+    @property
+    def dtype_code(self):
+        return _lib.MOE_E2M1 if self.fmt == "e2m1" else _lib.MOE_E4M3
 
     @property
     def rows(self):
@@ -71,41 +80,47 @@ def moe_mx_col_len(R: int, E: int) -> int:
     return int(_lib.load().moe_mx_col_len(R, E))
 
 
-def moe_mx_quantize(x, out: Optional[MXTensor] = None) -> MXTensor:
-    """Row copy of x [rows, n] (blocks of 32 along n)."""
+def _qname(base, fmt):
+    return base.replace("moe_mx_", "moe_mxfp4_") if fmt == "e2m1" else base
+
+
+def moe_mx_quantize(x, out: Optional[MXTensor] = None, fmt: str = "e4m3") -> MXTensor:
+    """Row copy of x [rows, n] (blocks of 32 along n); fmt "e4m3" (MXFP8) or
+    "e2m1" (MXFP4)."""
     x2 = x.reshape(-1, x.shape[-1])
     rows, n = x2.shape
-    out = MXTensor(rows, n, x.device) if out is None else out
-    check(_lib.load().moe_mx_quantize(_p(x2), _dtype(x), rows, n, _mx(out), _stream()),
-          "moe_mx_quantize")
+    out = MXTensor(rows, n, x.device, fmt=fmt) if out is None else out
+    name = _qname("moe_mx_quantize", out.fmt)
+    check(getattr(_lib.load(), name)(_p(x2), _dtype(x), rows, n, _mx(out), _stream()), name)
     return out
 
 
-def moe_mx_quantize_transpose(x, out: Optional[MXTensor] = None) -> MXTensor:
+def moe_mx_quantize_transpose(x, out: Optional[MXTensor] = None, fmt: str = "e4m3") -> MXTensor:
     """Transposed copy of x [B, rows, n]: row b*n + c = column c of x[b], blocked along rows."""
     B, rows, n = x.shape
-    out = MXTensor(B * n, rows, x.device) if out is None else out
-    check(_lib.load().moe_mx_quantize_transpose(_p(x), _dtype(x), B, rows, n, _mx(out),
-                                                _stream()),
-          "moe_mx_quantize_transpose")
+    out = MXTensor(B * n, rows, x.device, fmt=fmt) if out is None else out
+    name = _qname("moe_mx_quantize_transpose", out.fmt)
+    check(getattr(_lib.load(), name)(_p(x), _dtype(x), B, rows, n, _mx(out), _stream()), name)
     return out
 
 
 def moe_mx_quantize_experts(x, offsets, pad_offsets, R, *, src_row=None, row_map=None,
                             topk_w=None, want_row=True, want_col=True, row_out=None,
-                            col_out=None):
+                            col_out=None, fmt: str = "e4m3"):
     """Row and/or expert-segmented column copies of v[r] = x[src_row[r]] (* gate)."""
     n = x.shape[1]
     E = offsets.shape[0] - 1
     k = row_map.shape[1] if row_map is not None else 0
     if want_row and row_out is None:
-        row_out = MXTensor(R, n, x.device)
+        row_out = MXTensor(R, n, x.device, fmt=fmt)
     if want_col and col_out is None:
-        col_out = MXTensor(n, moe_mx_col_len(R, E), x.device)
-    check(_lib.load().moe_mx_quantize_experts(
+        col_out = MXTensor(n, moe_mx_col_len(R, E), x.device, fmt=fmt)
+    fmt = (row_out if want_row else col_out).fmt
+    name = _qname("moe_mx_quantize_experts", fmt)
+    check(getattr(_lib.load(), name)(
         _p(x), _dtype(x), _p(src_row), _p(row_map), _p(topk_w), k, _p(offsets),
         _p(pad_offsets), E, R, n, _mx(row_out if want_row else None),
-        _mx(col_out if want_col else None), _stream()), "moe_mx_quantize_experts")
+        _mx(col_out if want_col else None), _stream()), name)
     return (row_out if want_row else None), (col_out if want_col else None)
 
 
@@ -202,12 +217,12 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
         n1 = 2 * f
         dev = xp.data.device
         if want_row and a_row is None:
-            a_row = MXTensor(R, f, dev)
+            a_row = MXTensor(R, f, dev, fmt=xp.fmt)
         if want_col and a_col is None:
-            a_col = MXTensor(f, moe_mx_col_len(R, E), dev)
+            a_col = MXTensor(f, moe_mx_col_len(R, E), dev, fmt=xp.fmt)
         if save_h and h_out is None:
             h_out = torch.empty((R, n1), dtype=torch.bfloat16, device=dev)
-        args = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), _lib.MOE_E4M3, None, None, None,
+        args = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), xp.dtype_code, None, None, None,
                                _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                                _p(h_out) if save_h else None, None, max_cus, _mx(xp), _mx(w1p),
                                _mx(a_row if want_row else None),
@@ -240,7 +255,7 @@ def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0, E=None, N=
     if isinstance(a, MXTensor):
         R, K = a.rows, a.ld
         y = torch.empty((R, N), dtype=torch.bfloat16, device=a.data.device) if y is None else y
-        args = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), _lib.MOE_E4M3, None, None, None,
+        args = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), a.dtype_code, None, None, None,
                                 _p(offsets), E, R, N, K, _p(y), max_cus, _mx(a), _mx(w))
         check(_lib.load().moe_grouped_gemm_fwd(ctypes.byref(args), _stream()),
               "moe_grouped_gemm_fwd")
@@ -267,10 +282,10 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
         f = n1 // 2
         dev = h.device
         if want_row and dh_row is None:
-            dh_row = MXTensor(R, n1, dev)
+            dh_row = MXTensor(R, n1, dev, fmt=dy.fmt)
         if want_col and dh_col is None:
-            dh_col = MXTensor(n1, moe_mx_col_len(R, E), dev)
-        args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), _lib.MOE_E4M3, None, None, _p(h),
+            dh_col = MXTensor(n1, moe_mx_col_len(R, E), dev, fmt=dy.fmt)
+        args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), dy.dtype_code, None, None, _p(h),
                                _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                                None, max_cus, _mx(dy), _mx(w2), _mx(dh_row if want_row else None),
                                _mx(dh_col if want_col else None), _p(pad_offsets))
@@ -305,14 +320,14 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
             R, N = g.rows, g.ld
             out = torch.empty((R, K), dtype=torch.bfloat16, device=dev) if out is None else out
             m = _lib.MOE_BWD_DGRAD
-            args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_E4M3, m, None, None,
+            args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), g.dtype_code, m, None, None,
                                     None, _p(offsets), E, R, N, K, _p(out), None, 0, max_cus,
                                     _mx(g), None, _mx(w), None)
         elif mode == "wgrad":
             N, K = g.rows, a.rows
             out = torch.empty((E, N, K), dtype=torch.float32, device=dev) if out is None else out
             m = _lib.MOE_BWD_WGRAD
-            args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _lib.MOE_E4M3, m, None, None,
+            args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), g.dtype_code, m, None, None,
                                     None, _p(offsets), E, R, N, K, _p(out), None, int(accumulate),
                                     max_cus, _mx(g), _mx(a), None, _p(pad_offsets))
         else:

@@ -47,7 +47,7 @@ class MoEConfig:
     E: int                    # experts (local to this GPU)
     k: int                    # experts per token
     dtype: str = "bf16"       # storage dtype of activations / weights: "bf16" | "f32"
-    gemm: str = "bf16"        # GEMM operand precision: "bf16" | "f32" | "mxfp8"
+    gemm: str = "bf16"        # GEMM operand precision: "bf16" | "f32" | "mxfp8" | "mxfp4"
     score: str = "softmax"    # "softmax" | "sigmoid"
     normalize: bool = True    # renormalise the selected gates to sum to 1
     act: str = "swiglu"       # "swiglu" | "geglu" | "srelu"
@@ -104,6 +104,10 @@ WORKLOADS = {
     # Same shard with MXFP8 GEMM operands.
     "dsv3_mxfp8_fwdbwd": MoEConfig("dsv3_mxfp8_fwdbwd", T=16384, d=7168, f=2048, E=32, k=8,
                                    gemm="mxfp8", score="sigmoid", zipf=1.5, forced_empty=2,
+                                   forced_mode="top", seed=4, backward=True),
+    # Same shard with MXFP4 GEMM operands.
+    "dsv3_mxfp4_fwdbwd": MoEConfig("dsv3_mxfp4_fwdbwd", T=16384, d=7168, f=2048, E=32, k=8,
+                                   gemm="mxfp4", score="sigmoid", zipf=1.5, forced_empty=2,
                                    forced_mode="top", seed=4, backward=True),
 }
 

@@ -260,7 +260,13 @@ class ChainMX:
 
     def __init__(self, cfg, inp, idx, w, offsets, pad, src_row):
         from oracle import mx as omx
-        self.q = omx
+        fmt = "e2m1" if cfg.gemm == "mxfp4" else "e4m3"
+
+        class _Q:            # the oracle's QDQ in this workload's element format
+            @staticmethod
+            def mx_qdq(v, axis):
+                return omx.mx_qdq(v, axis, fmt=fmt)
+        self.q = _Q
         self.cfg, self.idx, self.w = cfg, idx, w
         self.x = _f32(inp["x"])
         self.W1 = inp["W1"]
@@ -335,11 +341,13 @@ def _tok_qdq(q, v):
 
 
 @pytest.mark.timeout(900)
-def test_fullsize_mxfp8_sampled():
-    """dsv3_mxfp8_fwdbwd at full size: sampled token rows of out and dX, and
-    weight-gradient columns of a heavy and a light expert, against the
-    oracle's MXFP8 chain; routing, offsets and padded offsets bit-exact."""
-    cfg = synth.WORKLOADS["dsv3_mxfp8_fwdbwd"]
+@pytest.mark.parametrize("name", ["dsv3_mxfp8_fwdbwd", "dsv3_mxfp4_fwdbwd"])
+def test_fullsize_mx_sampled(name):
+    """dsv3_mxfp8_fwdbwd / dsv3_mxfp4_fwdbwd at full size: sampled token rows
+    of out and dX, and weight-gradient columns of a heavy and a light expert,
+    against the oracle's MX chain in the same element format; routing, offsets
+    and padded offsets bit-exact."""
+    cfg = synth.WORKLOADS[name]
     note(f"full-size {cfg.name}: T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
     from ragged_grouped_gemm_amd import ops
     from ragged_grouped_gemm_amd.layer import MoEFFN
@@ -347,10 +355,10 @@ def test_fullsize_mxfp8_sampled():
     t = lambda a: synth.to_torch(a, "cuda")
     x, lg, dout = t(inp["x"]), t(inp["logits"]), t(inp["dOut"])
     W1p, _ = ops.moe_repack_glu_weights(t(inp["W1"]))
-    Wm = MoEFFN.mx_weights(W1p, t(inp["W2"]))
+    Wm = MoEFFN.mx_weights(W1p, t(inp["W2"]), cfg.gemm)
     del W1p
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, score=cfg.score, normalize=cfg.normalize,
-               gemm="mxfp8")
+               gemm=cfg.gemm)
     L.forward(x, lg, Wm, None)
     L.backward(dout, lg, Wm, None)
     torch.cuda.synchronize()
