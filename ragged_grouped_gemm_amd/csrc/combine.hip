@@ -70,6 +70,97 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
   }
 }
 
+// The same two kernels for a compile-time k: a lane issues the loads of all k
+// rows of a chunk (and, backward, reads d_out once) before using any, so each
+// lane keeps k + 1 loads in flight.  Sums run in the same order as above, so
+// the results are identical.
+template <class EL, int K>
+__global__ void __launch_bounds__(256) combine_kernel_k(const u32x4* __restrict__ y,
+                                                        const int32_t* __restrict__ row_map,
+                                                        const float* __restrict__ w, int T, int R,
+                                                        int chunks, u32x4* __restrict__ out) {
+  constexpr int V = EL::VEC;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  int rows[K];
+  float ws[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int r = row_map[(size_t)t * K + j];
+    rows[j] = (r < 0 || r >= R) ? 0 : r;
+    ws[j] = w ? w[(size_t)t * K + j] : 1.0f;
+  }
+  for (int c = lane; c < chunks; c += 64) {
+    u32x4 raw[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) raw[j] = y[(size_t)rows[j] * chunks + c];
+    float acc[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float v[V];
+      unpack_chunk(raw[j], v, EL());
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = fmaf(ws[j], v[q], acc[q]);
+    }
+    out[(size_t)t * chunks + c] = pack_chunk(acc, EL());
+  }
+}
+
+template <class EL, int K>
+__global__ void __launch_bounds__(256) combine_bwd_kernel_k(
+    const u32x4* __restrict__ dout, const u32x4* __restrict__ y,
+    const int32_t* __restrict__ row_map, const float* __restrict__ w, int T, int R, int chunks,
+    u32x4* __restrict__ dy, float* __restrict__ dw) {
+  constexpr int V = EL::VEC;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  int rows[K];
+  float ws[K], part[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int r = row_map[(size_t)t * K + j];
+    rows[j] = (r < 0 || r >= R) ? 0 : r;
+    ws[j] = w[(size_t)t * K + j];
+    part[j] = 0.0f;
+  }
+  for (int c = lane; c < chunks; c += 64) {
+    const u32x4 graw = dout[(size_t)t * chunks + c];
+    u32x4 raw[K];
+    if (dw) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) raw[j] = y[(size_t)rows[j] * chunks + c];
+    }
+    float g[V];
+    unpack_chunk(graw, g, EL());
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (dw) {
+        float v[V];
+        unpack_chunk(raw[j], v, EL());
+#pragma unroll
+        for (int q = 0; q < V; ++q) part[j] = fmaf(g[q], v[q], part[j]);
+      }
+      if (dy) {
+        float o[V];
+#pragma unroll
+        for (int q = 0; q < V; ++q) o[q] = ws[j] * g[q];
+        dy[(size_t)rows[j] * chunks + c] = pack_chunk(o, EL());
+      }
+    }
+  }
+  if (dw) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float tot = wave_sum(part[j]);
+      if (lane == 0) dw[(size_t)t * K + j] = tot;
+    }
+  }
+}
+
 // Bias gradient of a grouped linear map: db[e][n] = sum over the rows of
 // segment e of g[r][n], float32, rows summed in order (deterministic).
 // grid: (ceil(N / 256), E); each thread owns one column.
@@ -153,14 +244,33 @@ moe_status_t moe_unpermute_combine(const void* y, int dtype, const int32_t* row_
   int chunks = (int)(d * dtype_size(dtype) / 16);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   dim3 grid((T + 3) / 4);
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<BF16>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const u32x4*>(y), row_map, topk_w, T, k, T * k, chunks,
-                       reinterpret_cast<u32x4*>(out));
+  const u32x4* yy = reinterpret_cast<const u32x4*>(y);
+  u32x4* oo = reinterpret_cast<u32x4*>(out);
+  const bool bf = dtype == MOE_BF16;
+#define MOE_COMBINE_K(KK)                                                                  \
+  case KK:                                                                                 \
+    if (bf)                                                                                \
+      hipLaunchKernelGGL((combine_kernel_k<BF16, KK>), grid, dim3(256), 0, s, yy, row_map, \
+                         topk_w, T, T * k, chunks, oo);                                    \
+    else                                                                                   \
+      hipLaunchKernelGGL((combine_kernel_k<F32, KK>), grid, dim3(256), 0, s, yy, row_map,  \
+                         topk_w, T, T * k, chunks, oo);                                    \
+    return launch_status();
+  switch (k) {
+    MOE_COMBINE_K(1)
+    MOE_COMBINE_K(2)
+    MOE_COMBINE_K(4)
+    MOE_COMBINE_K(8)
+    default:
+      break;
+  }
+#undef MOE_COMBINE_K
+  if (bf)
+    hipLaunchKernelGGL(combine_kernel<BF16>, grid, dim3(256), 0, s, yy, row_map, topk_w, T, k,
+                       T * k, chunks, oo);
   else
-    hipLaunchKernelGGL(combine_kernel<F32>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const u32x4*>(y), row_map, topk_w, T, k, T * k, chunks,
-                       reinterpret_cast<u32x4*>(out));
+    hipLaunchKernelGGL(combine_kernel<F32>, grid, dim3(256), 0, s, yy, row_map, topk_w, T, k,
+                       T * k, chunks, oo);
   return launch_status();
 }
 
@@ -175,16 +285,34 @@ moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dty
   int chunks = (int)(d * dtype_size(dtype) / 16);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   dim3 grid((T + 3) / 4);
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd_kernel<BF16>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const u32x4*>(d_out), reinterpret_cast<const u32x4*>(y),
-                       row_map, topk_w, T, k, T * k, chunks, reinterpret_cast<u32x4*>(d_y),
-                       d_topk_w);
+  const u32x4* gg = reinterpret_cast<const u32x4*>(d_out);
+  const u32x4* yy = reinterpret_cast<const u32x4*>(y);
+  u32x4* dd = reinterpret_cast<u32x4*>(d_y);
+  const bool bf = dtype == MOE_BF16;
+#define MOE_COMBINE_BWD_K(KK)                                                                 \
+  case KK:                                                                                    \
+    if (bf)                                                                                   \
+      hipLaunchKernelGGL((combine_bwd_kernel_k<BF16, KK>), grid, dim3(256), 0, s, gg, yy,     \
+                         row_map, topk_w, T, T * k, chunks, dd, d_topk_w);                    \
+    else                                                                                      \
+      hipLaunchKernelGGL((combine_bwd_kernel_k<F32, KK>), grid, dim3(256), 0, s, gg, yy,      \
+                         row_map, topk_w, T, T * k, chunks, dd, d_topk_w);                    \
+    return launch_status();
+  switch (k) {
+    MOE_COMBINE_BWD_K(1)
+    MOE_COMBINE_BWD_K(2)
+    MOE_COMBINE_BWD_K(4)
+    MOE_COMBINE_BWD_K(8)
+    default:
+      break;
+  }
+#undef MOE_COMBINE_BWD_K
+  if (bf)
+    hipLaunchKernelGGL(combine_bwd_kernel<BF16>, grid, dim3(256), 0, s, gg, yy, row_map, topk_w,
+                       T, k, T * k, chunks, dd, d_topk_w);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<F32>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const u32x4*>(d_out), reinterpret_cast<const u32x4*>(y),
-                       row_map, topk_w, T, k, T * k, chunks, reinterpret_cast<u32x4*>(d_y),
-                       d_topk_w);
+    hipLaunchKernelGGL(combine_bwd_kernel<F32>, grid, dim3(256), 0, s, gg, yy, row_map, topk_w,
+                       T, k, T * k, chunks, dd, d_topk_w);
   return launch_status();
 }
 

@@ -112,12 +112,24 @@ __global__ void __launch_bounds__(256)
 }
 
 // Row and column copies of one group of 32 expert-ordered rows x 256 columns
-// in one pass.  The workgroup loads the tile with 16-byte loads (gathered rows,
-// gate product applied) into LDS, row stride 260 floats; thread t then
-// quantizes row t % 32 of 32-column block t / 32 into the row copy (rows of a
-// wave read one block of 32 different rows: distinct banks) and column t over
-// the 32 rows into the column copy (consecutive columns: distinct banks).
-constexpr int TILE_LD = 260;
+// in one pass.  The workgroup copies the tile's raw 16-byte chunks (gathered
+// rows) into LDS, row stride TILE_LD elements (bf16: 528 bytes, fp32: 1040,
+// both 16 mod 256, so the 32 rows of a block read sit in distinct banks); the
+// gate product is applied as values leave LDS.  Thread t then quantizes row
+// t % 32 of 32-column block t / 32 into the row copy and column t over the 32
+// rows into the column copy.  Staging the input type rather than float32
+// halves the LDS of a bf16 workgroup, which doubles the workgroups a compute
+// unit holds and so the loads in flight.
+template <class S>
+struct TileLd;
+template <>
+struct TileLd<uint16_t> {
+  static constexpr int LD = 264;
+};
+template <>
+struct TileLd<float> {
+  static constexpr int LD = 260;
+};
 
 template <class EL, class F>
 __global__ void __launch_bounds__(256)
@@ -127,8 +139,10 @@ __global__ void __launch_bounds__(256)
                      const float* __restrict__ topk_w, int k, uint8_t* __restrict__ rcodes,
                      uint8_t* __restrict__ rscales, long long rld, uint8_t* __restrict__ ccodes,
                      uint8_t* __restrict__ cscales, long long cld, long long ngroups) {
-  constexpr int V = EL::VEC;               // elements per 16-byte load
-  __shared__ float tile[32 * TILE_LD];
+  typedef typename EL::storage S;
+  constexpr int V = EL::VEC;               // elements per 16-byte chunk
+  constexpr int TLD = TileLd<S>::LD;
+  __shared__ __attribute__((aligned(16))) S tile[32 * TLD];
   __shared__ long long s_src[32];
   __shared__ float s_w[32];
   __shared__ int s_row[32];                // routed row of tile row i (or -1)
@@ -151,29 +165,24 @@ __global__ void __launch_bounds__(256)
       s_w[tid] = (ok && topk_w) ? row_gate(row_map, topk_w, k, sr, r) : 1.0f;
     }
     __syncthreads();
-    // load: 32 rows x 256 columns, 16 bytes per thread per step
-    constexpr int PER_ROW = 256 / V;                 // loads per tile row
+    // copy: 32 rows x 256 columns, one 16-byte chunk per thread per step
+    constexpr int PER_ROW = 256 / V;                 // chunks per tile row
     constexpr int STEPS = 32 * PER_ROW / 256;
+    u32x4 raw[STEPS];
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int idx = st * 256 + tid;
       const int i = idx / PER_ROW, cc = (idx % PER_ROW) * V;
-      float v[V];
       const long long sr = s_src[i];
-      if (sr >= 0 && c0 + cc < n) {
-        unpack_chunk(*reinterpret_cast<const u32x4*>(x + sr * n + c0 + cc), v, EL());
-        if (topk_w) {
+      raw[st] = (sr >= 0 && c0 + cc < n)
+                    ? *reinterpret_cast<const u32x4*>(x + sr * n + c0 + cc)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-          for (int q = 0; q < V; ++q) v[q] *= s_w[i];
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < V; ++q) v[q] = 0.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < V; q += 4)
-        *reinterpret_cast<f32x4*>(tile + i * TILE_LD + cc + q) =
-            f32x4{v[q], v[q + 1], v[q + 2], v[q + 3]};
+    for (int st = 0; st < STEPS; ++st) {
+      const int idx = st * 256 + tid;
+      const int i = idx / PER_ROW, cc = (idx % PER_ROW) * V;
+      *reinterpret_cast<u32x4*>(tile + i * TLD + cc) = raw[st];
     }
     __syncthreads();
     float v[32];
@@ -183,13 +192,13 @@ __global__ void __launch_bounds__(256)
       const int i = tid & 31, b = tid >> 5, col = c0 + 32 * b;
       const int r = s_row[i];
       if (rcodes && r >= 0 && col < n) {
+        const float wi = s_w[i];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(tile + i * TILE_LD + 32 * b + 4 * q);
-          v[4 * q] = t[0];
-          v[4 * q + 1] = t[1];
-          v[4 * q + 2] = t[2];
-          v[4 * q + 3] = t[3];
+        for (int q = 0; q < 32 / V; ++q) {
+          float t[V];
+          unpack_chunk(*reinterpret_cast<const u32x4*>(tile + i * TLD + 32 * b + V * q), t, EL());
+#pragma unroll
+          for (int e = 0; e < V; ++e) v[V * q + e] = topk_w ? t[e] * wi : t[e];
         }
         const uint32_t sc = mx_quant32<F>(v, w8);
         store_block<F>(rcodes + (size_t)r * (rld / 32 * F::BYTES) + col / 32 * F::BYTES, w8);
@@ -199,7 +208,10 @@ __global__ void __launch_bounds__(256)
     // column copy: column t over the 32 rows
     if (ccodes && c0 + tid < n) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = tile[i * TILE_LD + tid];
+      for (int i = 0; i < 32; ++i) {
+        const float t = ld1(tile + i * TLD + tid);
+        v[i] = topk_w ? t * s_w[i] : t;
+      }
       const uint32_t sc = mx_quant32<F>(v, w8);
       store_block<F>(ccodes + (size_t)(c0 + tid) * (cld / 32 * F::BYTES) + prow0 / 32 * F::BYTES,
                      w8);
