@@ -489,7 +489,7 @@ class LayerSpec:
     """Options of the layer (what the configs vary)."""
 
     def __init__(self, k, score="softmax", normalize=True, act="swiglu", clamp=0.0,
-                 alpha=1.0, gelu_tanh=False, store="bf16", gemm="bf16"):
+                 alpha=1.0, gelu_tanh=False, store="bf16", gemm="bf16", mx_dxp=False):
         self.k = k
         self.score = score
         self.normalize = normalize
@@ -500,6 +500,10 @@ class LayerSpec:
         self.store = store      # dtype of every stored activation: "bf16", "f32" or "f64"
         self.gemm = gemm        # GEMM operands: "bf16"/"f32" (the stored tensors), "mxfp8"
         #                         or "mxfp4" (same quantization points, E2M1 elements)
+        # MX variants: FC1's dgrad output dXp is stored as an MX row copy (blocks
+        # along d, from the exact values) instead of bf16, as for a quantized
+        # backward dispatch; the unpermute-sum then adds the decoded rows
+        self.mx_dxp = mx_dxp
 
     @property
     def gated(self):
@@ -606,7 +610,7 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
         dH_s = rnd(dH)
         dW1, db1 = grouped_wgrad(dH_s, fwd["xp"], offsets, with_bias=True)
         dXp = grouped_dgrad(dH_s, W1, offsets)
-    dXp_s = rnd(dXp)
+    dXp_s = _mx.mx_qdq(dXp, 1, fmt=spec.fmt) if (q and spec.mx_dxp) else rnd(dXp)
     dX = combine(dXp_s, row_map, None)
     out = dict(dY=dY_s, dgate=dgate, dlogits=dlogits, dA=dA, dH=dH_s, dW2=dW2, dXp=dXp_s,
                dW1=dW1, dX=rnd(dX), dY_exact=dY, dH_exact=dH, dXp_exact=dXp, dX_exact=dX)

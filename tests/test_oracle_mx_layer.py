@@ -12,7 +12,7 @@ stored values) against the reading in the oracle's header:
   FC1:  QDQ_d(Xp) . QDQ_d(W1)^T -> H (bf16 kept) -> A exact
   FC2:  QDQ_f(A) . QDQ_f(W2)^T -> Y (bf16) -> out = sum_j w Y (bf16)
   bwd:  dY = w dOut; dA = QDQ_d(dY) . QDQ_d(W2); dH exact from bf16 H;
-        dXp = QDQ_2f(dH) . QDQ_2f(W1) (bf16); dX = sum_j dXp (bf16);
+        dXp = QDQ_2f(dH) . QDQ_2f(W1) (bf16, or QDQ_d of it with mx_dxp); dX = sum_j dXp (bf16);
         dW2 = QDQ_tok(dY)^T QDQ_tok(A);  dW1 = QDQ_tok(dH)^T QDQ_tok(Xp).
 
 torch's cast rounds float64 through float32 first, which differs from a
@@ -120,7 +120,8 @@ def brute(x, logits, W1, W2, dout, spec):
         dA = qlast(dY) @ W2q_d[e]
         dg, dl = om.glu_backward(dA, Hs[:, :F], Hs[:, F:], spec.act)
         dH = np.concatenate([dg, dl], 1)
-        dXp = bf16(qlast(dH) @ W1q_2f[e])
+        dXp = qlast(dH) @ W1q_2f[e]
+        dXp = qlast(dXp) if spec.mx_dxp else bf16(dXp)
         for r, (t, j) in enumerate(assign):
             dX[t] += dXp[r]
         dW2[e] = qdq_tokens(dY).T @ qdq_tokens(A)
@@ -137,10 +138,11 @@ def case():
     return cfg, f(inp["x"]), inp["logits"], f(inp["W1"]), f(inp["W2"]), f(inp["dOut"])
 
 
-@pytest.mark.parametrize("gemm,fmt", [("mxfp8", "e4m3"), ("mxfp4", "e2m1")])
-def test_mx_chain_matches_brute_force(case, gemm, fmt):
+@pytest.mark.parametrize("gemm,fmt,mx_dxp", [("mxfp8", "e4m3", False), ("mxfp4", "e2m1", False),
+                                            ("mxfp8", "e4m3", True), ("mxfp4", "e2m1", True)])
+def test_mx_chain_matches_brute_force(case, gemm, fmt, mx_dxp):
     cfg, x, logits, W1, W2, dout = case
-    spec = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16", gemm=gemm)
+    spec = om.LayerSpec(K, "sigmoid", True, "swiglu", store="bf16", gemm=gemm, mx_dxp=mx_dxp)
     fwd = om.layer_forward(x, logits, W1, W2, spec=spec)
     bwd = om.layer_backward(fwd, dout, logits, W1, W2, spec=spec)
     _fmt[0] = fmt
