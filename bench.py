@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--permute", choices=["fused", "copy"], default="fused",
                     help="bf16 / fp32 workloads: FC1 and FC1 wgrad read x through src_row "
                          "(fused) or a materialized permuted copy (copy)")
+    ap.add_argument("--mx-dxp", action="store_true",
+                    help="MX workloads: FC1's dgrad writes dXp as an MX row copy and dX is "
+                         "summed from it (quantized plain-GEMM output)")
     ap.add_argument("--recompute", action="store_true",
                     help="bf16 / fp32 training workloads: H is not kept from the forward, the "
                          "backward runs FC1 + GLU again (its FLOP are not counted in the metric)")
@@ -191,7 +194,7 @@ def main():
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
-               recompute=args.recompute)
+               recompute=args.recompute, mx_dxp=args.mx_dxp)
     permute = "fused" if L.fuse_permute else "copy"
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
@@ -265,6 +268,7 @@ def main():
                    "k": cfg.k, "routed_rows": cfg.R, "score": cfg.score, "act": cfg.act,
                    "permute": "mx_quantize_gather" if mx else permute,
                    "recompute_fc1": bool(args.recompute),
+                   "mx_dxp": bool(args.mx_dxp),
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "gemm_only_tflops": round(total_flops / gemm_ms / 1e9, 2),

@@ -239,6 +239,11 @@ typedef struct {
    * y is bf16; no bias. */
   const moe_mx_t* a_mx;
   const moe_mx_t* w_mx;
+  /* MX operands only (nullable): y written as an MX row copy [R, N] in the
+   * operands' element format (blocks along N, quantized from the float32
+   * products; N a multiple of 32) instead of bf16 -- the quantized GEMM
+   * output of a low-precision dispatch; y may then be NULL. */
+  moe_mx_t* y_mx;
 } moe_gemm_fwd_args_t;
 moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* args, void* stream);
 
@@ -311,6 +316,12 @@ typedef struct {
    * Same limits as moe_glu_fwd_args_t.src_row. */
   const int32_t* a_src_row;
   int a_src_rows;
+  /* DGRAD with MX operands (nullable): da written as an MX row copy [R, K]
+   * in the operands' element format (blocks along K, from the float32
+   * products; K a multiple of 32) instead of bf16, e.g. dXp for a quantized
+   * dispatch backward (moe_unpermute_combine_mx sums it); out may then be
+   * NULL. */
+  moe_mx_t* out_mx;
 } moe_gemm_bwd_args_t;
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream);
 
@@ -400,6 +411,14 @@ moe_status_t moe_mxfp4_quantize_experts(const void* x, int dtype, const int32_t*
 moe_status_t moe_unpermute_combine(const void* y, int dtype, const int32_t* row_map,
                                    const float* topk_w, int T, int k, int d, void* out,
                                    void* stream);
+
+/* a12 from MX rows: out[t] = sum_{j<k} (topk_w ? topk_w[t,j] : 1) * decode(y)[row_map[t,j]],
+ * decode(y) = codes x block scale, summed in float32 in slot order, rounded
+ * once to out_dtype (F32 or BF16).  y [T*k, d] MX row copy of element format
+ * y_dtype (MOE_E4M3 or MOE_E2M1), d a multiple of 32; out [T, d]. */
+moe_status_t moe_unpermute_combine_mx(const moe_mx_t* y, int y_dtype, const int32_t* row_map,
+                                      const float* topk_w, int T, int k, int d, void* out,
+                                      int out_dtype, void* stream);
 
 /* a6.  Backward of the combine:
  *   d_y[row_map[t,j]]  = topk_w[t,j] * d_out[t]        (dtype, rounded once)

@@ -45,7 +45,7 @@ class GemmFwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", c_size_t), ("dtype", c_int), ("a", c_void_p), ("w", c_void_p),
                 ("b", c_void_p), ("offsets", c_void_p), ("E", c_int), ("R", c_int),
                 ("N", c_int), ("K", c_int), ("y", c_void_p), ("max_cus", c_int),
-                ("a_mx", _PMX), ("w_mx", _PMX)]
+                ("a_mx", _PMX), ("w_mx", _PMX), ("y_mx", _PMX)]
 
 
 class GluBwdArgs(ctypes.Structure):
@@ -63,7 +63,7 @@ class GemmBwdArgs(ctypes.Structure):
                 ("R", c_int), ("N", c_int), ("K", c_int), ("out", c_void_p), ("db", c_void_p),
                 ("accumulate", c_int), ("max_cus", c_int), ("g_mx", _PMX), ("a_mx", _PMX),
                 ("w_mx", _PMX), ("pad_offsets", c_void_p), ("a_src_row", c_void_p),
-                ("a_src_rows", c_int)]
+                ("a_src_rows", c_int), ("out_mx", _PMX)]
 
 
 _SIGS = {
@@ -94,6 +94,8 @@ _SIGS = {
     "moe_mx_quantize_experts": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,
                                         c_void_p, c_void_p, c_int, c_int, c_int, _PMX, _PMX,
                                         c_void_p]),
+    "moe_unpermute_combine_mx": (c_int, [_PMX, c_int, c_void_p, c_void_p, c_int, c_int, c_int,
+                                         c_void_p, c_int, c_void_p]),
     "moe_mxfp4_quantize": (c_int, [c_void_p, c_int, ctypes.c_int64, c_int, _PMX, c_void_p]),
     "moe_mxfp4_quantize_transpose": (c_int, [c_void_p, c_int, c_int, c_int, c_int, _PMX,
                                              c_void_p]),

@@ -1358,7 +1358,33 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     // ---- epilogue: lane holds rows (lane & 31) + 32 i, columns 32 j + 8 g + 4 h + q ----
     typedef typename OutT<EL>::type SO;
     const int cw = n0 + wn * C::WTN + 4 * (lane >> 5);  // column of the lane's first value
-    if constexpr (MX && (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))) {
+    bool mx_store = false;  // plain product written as an MX row copy instead of C
+    if constexpr (MX && EPI == EPI_STORE && GROUP == RAGGED_M) mx_store = p.mxr != nullptr;
+    if (mx_store) {
+      if constexpr (MX && EPI == EPI_STORE && GROUP == RAGGED_M) {
+        // each 32 x 32 block passes through the wave's staging tile; lanes
+        // 0-31 quantize one row of it each (blocks of 32 columns)
+        float* Wt = reinterpret_cast<float*>(stage_ptr(nk + wave / C::STAGE_WAVES)) +
+                    (wave % C::STAGE_WAVES) * C::MX_STAGE_FLOATS;
+        static_for<0, TM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const int r0 = m0 + wm * C::WTM + 32 * i;
+          static_for<0, TN>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int cb = n0 + wn * C::WTN + 32 * j;
+            if (cb < p.N) {
+              float o[16];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[r] = acc[i][j][r];
+              mx_stage(Wt, lane, o);
+              wave_lds_sync();
+              mx_emit<typename EL::Fmt>(Wt, lane, p, r0, mlim, cb, 0, 0);
+              wave_lds_sync();
+            }
+          });
+        });
+      }
+    } else if constexpr (MX && (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))) {
       // every lane takes part (the tile is shared); rows past the segment are
       // zero in the column copy and skipped in the row copy.  The ring slot
       // after the last step's is free: its last reader passed the barrier of
@@ -1633,6 +1659,15 @@ using namespace moe;
 
 // An MXFP8 GEMM operand with reduction length K: ld a multiple of 128 (whole
 // scale words per k-step) and at least K.
+// An MX output field of an argument struct, or NULL when the caller's struct
+// predates it.
+template <class A>
+inline moe_mx_t* mx_out_field(const A* a, moe_mx_t* const A::*f) {
+  const size_t end = (size_t)(reinterpret_cast<const char*>(&(a->*f)) -
+                              reinterpret_cast<const char*>(a)) + sizeof(moe_mx_t*);
+  return a->struct_size >= end ? a->*f : nullptr;
+}
+
 // The gather index of an argument struct, or NULL when the caller's struct
 // predates the field.
 template <class A>
@@ -1724,10 +1759,12 @@ moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
 
 moe_status_t gemm_fwd_mx(const moe_gemm_fwd_args_t* a, hipStream_t s) {
   const int dt = a->dtype;
-  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_gemm_fwd_args_t));
+  MOE_CHECK_ARG(a->struct_size >= offsetof(moe_gemm_fwd_args_t, y_mx));
   MOE_CHECK_ARG(a->b == nullptr && a->K % 128 == 0);
   if (a->R == 0) return MOE_OK;
-  MOE_CHECK_ARG(a->offsets && a->y && aligned16(a->y));
+  moe_mx_t* ymx = mx_out_field(a, &moe_gemm_fwd_args_t::y_mx);
+  MOE_CHECK_ARG(a->offsets && (ymx ? mx_out_ok(ymx, a->N) && a->N % 32 == 0
+                                   : (a->y && aligned16(a->y))));
   MOE_CHECK_ARG(mx_in_ok(a->a_mx, a->K) && mx_in_ok(a->w_mx, a->K));
   GemmArgs p = zero_args();
   set_mx_a(p, a->a_mx, dt);
@@ -1739,6 +1776,7 @@ moe_status_t gemm_fwd_mx(const moe_gemm_fwd_args_t* a, hipStream_t s) {
   p.K = a->K / mx_epb(dt);
   p.c = a->y;
   p.ldc = a->N;
+  set_mx_out(p, ymx, nullptr, nullptr);
   return dispatch_mx<RAGGED_M, EPI_STORE>(p, big_ragged_m(a->R, a->E, a->N), a->max_cus, s, dt);
 }
 
@@ -1786,6 +1824,9 @@ moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
     MOE_CHECK_ARG(a->N % 128 == 0);
     if (a->R == 0) return MOE_OK;
     MOE_CHECK_ARG(a->offsets && mx_in_ok(a->g_mx, a->N) && mx_in_ok(a->w_mx, a->N));
+    moe_mx_t* omx = mx_out_field(a, &moe_gemm_bwd_args_t::out_mx);
+    MOE_CHECK_ARG(omx ? mx_out_ok(omx, a->K) && a->K % 32 == 0 : (a->out && aligned16(a->out)));
+    set_mx_out(p, omx, nullptr, nullptr);
     set_mx_a(p, a->g_mx, dt);
     set_mx_b(p, a->w_mx, a->K, dt);
     p.offsets = a->offsets;
@@ -1799,7 +1840,8 @@ moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
   }
   // dw[e] [N, K] = g_col[:, seg e] @ a_col[:, seg e]^T; the k ranges are the
   // padded segments, so the offsets table is pad_offsets and R its bound
-  MOE_CHECK_ARG(a->db == nullptr && a->pad_offsets);
+  MOE_CHECK_ARG(a->db == nullptr && a->pad_offsets && a->out && aligned16(a->out));
+  MOE_CHECK_ARG(!mx_out_field(a, &moe_gemm_bwd_args_t::out_mx));
   const long long L = moe_mx_col_len(a->R, a->E);
   MOE_CHECK_ARG(mx_in_ok(a->g_mx, L) && mx_in_ok(a->a_mx, L));
   MOE_CHECK_ARG(L <= 0x7fffffff);
@@ -1875,6 +1917,7 @@ moe_status_t moe_grouped_gemm_fwd(const moe_gemm_fwd_args_t* a, void* stream) {
   MOE_CHECK_ARG(a->N > 0 && a->K > 0 && a->N % 8 == 0 && a->K % 8 == 0);
   if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
     return gemm_fwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  MOE_CHECK_ARG(!mx_out_field(a, &moe_gemm_fwd_args_t::y_mx));
   if (a->R == 0) return MOE_OK;
   MOE_CHECK_ARG(a->a && a->w && a->offsets && a->y);
   MOE_CHECK_ARG(aligned16(a->a) && aligned16(a->w) && aligned16(a->y) && aligned16(a->b));
@@ -1945,9 +1988,10 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
   MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS && a->R >= 0);
   MOE_CHECK_ARG(a->N > 0 && a->K > 0 && a->N % 8 == 0 && a->K % 8 == 0);
   MOE_CHECK_ARG(a->mode == MOE_BWD_DGRAD || a->mode == MOE_BWD_WGRAD);
-  MOE_CHECK_ARG(a->out && aligned16(a->out));
   if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
     return gemm_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
+  MOE_CHECK_ARG(a->out && aligned16(a->out));
+  MOE_CHECK_ARG(!mx_out_field(a, &moe_gemm_bwd_args_t::out_mx));
   MOE_CHECK_ARG(a->g && a->offsets && aligned16(a->g));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   GemmArgs p = zero_args();

@@ -221,6 +221,96 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Decoded element values (exact in float32).  E4M3: (1 + m/8) 2^(e-7), or
+// m 2^-9 for e = 0, NaN for S.1111.111; E2M1: (1 + m/2) 2^(e-1), or m/2.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if ((c & 0x7fu) == 0x7fu) v = __uint_as_float(0x7fc00000u);
+  return (c & 0x80u) ? -v : v;
+}
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float v = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return (c & 0x8u) ? -v : v;
+}
+// E8M0 scale 2^(s - 127) (s = 0 is the float32 subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+  return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
+}
+
+// Unpermute-sum of MX rows: one wave per token, a lane per 16 elements (half
+// a scale block): out[t] = sum_j w_j * decode(y[row_map[t, j]]) in float32 in
+// slot order.  K > 0 fixes k at compile time (all k rows' loads of a unit in
+// flight); K = 0 takes the run-time k.
+template <class F, int K, bool BF_OUT>
+__global__ void __launch_bounds__(256)
+    combine_mx_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                      long long ld, const int32_t* __restrict__ row_map,
+                      const float* __restrict__ w, int T, int R, int k_rt, int d,
+                      void* __restrict__ out) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int k = K > 0 ? K : k_rt;
+  const int units = d / 16;
+  const long long ldb = ld / 32 * F::BYTES;                  // code bytes per row
+  for (int u = lane; u < units; u += 64) {
+    float acc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll(K > 0 ? K : 1)
+    for (int j = 0; j < k; ++j) {
+      int r = row_map[(size_t)t * k + j];
+      r = (r < 0 || r >= R) ? 0 : r;
+      const float wj = w ? w[(size_t)t * k + j] : 1.0f;
+      const float sc = e8m0_value(scales[(size_t)r * (ld / 32) + u / 2]);
+      float v[16];
+      if constexpr (F::WORDS == 8) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(codes + (size_t)r * ldb + 16 * u);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = e4m3_value((c[q >> 2] >> (8 * (q & 3))) & 0xffu);
+      } else {
+        const u32x2 c = *reinterpret_cast<const u32x2*>(codes + (size_t)r * ldb + 8 * u);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = e2m1_value((c[q >> 3] >> (4 * (q & 7))) & 0xfu);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = fmaf(wj, v[q] * sc, acc[q]);
+    }
+    if constexpr (BF_OUT) {
+      u32x4* o = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (size_t)t * d + 16 * u);
+      o[0] = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+      o[1] = u32x4{pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
+                   pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15])};
+    } else {
+      f32x4* o = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)t * d + 16 * u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    }
+  }
+}
+
+template <class F, bool BF_OUT>
+void launch_combine_mx(const moe_mx_t* y, const int32_t* row_map, const float* w, int T, int k,
+                       int d, void* out, hipStream_t s) {
+  const dim3 grid((T + 3) / 4);
+  const int R = T * k;
+#define MOE_CMX(KK)                                                                            \
+  hipLaunchKernelGGL((combine_mx_kernel<F, KK, BF_OUT>), grid, dim3(256), 0, s, y->data,       \
+                     y->scale, (long long)y->ld, row_map, w, T, R, k, d, out)
+  switch (k) {
+    case 1: MOE_CMX(1); break;
+    case 2: MOE_CMX(2); break;
+    case 4: MOE_CMX(4); break;
+    case 8: MOE_CMX(8); break;
+    default: MOE_CMX(0); break;
+  }
+#undef MOE_CMX
+}
+
 bool mx_ok(const moe_mx_t* m) {
   return m && m->data && m->scale && m->ld > 0 && m->ld % 32 == 0 && aligned16(m->data);
 }
@@ -371,6 +461,26 @@ moe_status_t moe_mxfp4_quantize_experts(const void* x, int dtype, const int32_t*
                                         void* stream) {
   return mx_quantize_experts_impl<FmtE2M1>(x, dtype, src_row, row_map, topk_w, k, offsets,
                                            pad_offsets, E, R, n, row_out, col_out, stream);
+}
+
+moe_status_t moe_unpermute_combine_mx(const moe_mx_t* y, int y_dtype, const int32_t* row_map,
+                                      const float* topk_w, int T, int k, int d, void* out,
+                                      int out_dtype, void* stream) {
+  MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && d > 0 && d % 32 == 0);
+  MOE_CHECK_ARG(y_dtype == MOE_E4M3 || y_dtype == MOE_E2M1);
+  MOE_CHECK_ARG(out_dtype == MOE_BF16 || out_dtype == MOE_F32);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(mx_ok(y) && y->ld >= d && row_map && out && aligned16(out));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool bf = out_dtype == MOE_BF16;
+  if (y_dtype == MOE_E4M3) {
+    if (bf) launch_combine_mx<FmtE4M3, true>(y, row_map, topk_w, T, k, d, out, s);
+    else launch_combine_mx<FmtE4M3, false>(y, row_map, topk_w, T, k, d, out, s);
+  } else {
+    if (bf) launch_combine_mx<FmtE2M1, true>(y, row_map, topk_w, T, k, d, out, s);
+    else launch_combine_mx<FmtE2M1, false>(y, row_map, topk_w, T, k, d, out, s);
+  }
+  return launch_status();
 }
 
 }  // extern "C"

@@ -24,7 +24,8 @@ its inputs, at the price of one more FC1 GEMM (4·R·d·f FLOP) per backward;
 the gradients are bit-identical to the stored-H path.
 
 MXFP8 variant (``gemm="mxfp8"``; ``gemm="mxfp4"`` is the same with E2M1
-elements): every GEMM operand is an MXFP8 copy blocked
+elements; ``mx_dxp=True`` also writes FC1's dgrad output dXp as an MX row
+copy and sums dX from it): every GEMM operand is an MXFP8 copy blocked
 along that GEMM's reduction axis.  Xp and dY exist only as MXFP8 row and
 expert-segmented column copies written straight from x and d_out; FC1's
 epilogue writes A, and the dGLU epilogue dH, as the same two copies; H stays
@@ -59,12 +60,15 @@ class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
-                 recompute=False):
+                 recompute=False, mx_dxp=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
             raise ValueError(gemm)
         self.mx = gemm in ("mxfp8", "mxfp4")
         self.mx_fmt = "e2m1" if gemm == "mxfp4" else "e4m3"
+        if mx_dxp and not self.mx:
+            raise ValueError("mx_dxp applies to the MX variants")
+        self.mx_dxp = mx_dxp
         if recompute and (self.mx or not backward):
             raise ValueError("recompute applies to the bf16 / fp32 training layer")
         self.recompute = recompute
@@ -137,7 +141,7 @@ class MoEFFN:
             self.dlogits = z((T, E), f32)
             self.dY_row, self.dY_col = mx(R, d), mx(d, L)
             self.dH_row, self.dH_col = mx(R, n1), mx(n1, L)
-            self.dXp = z((R, d), bf)
+            self.dXp = mx(R, d) if self.mx_dxp else z((R, d), bf)
             self.dX = z((T, d), bf)
             self.dW1p = z((E, n1, d), f32)
             self.dW2 = z((E, d, f), f32)
@@ -271,14 +275,21 @@ class MoEFFN:
                                      out=self.dW2, E=E, R=R, pad_offsets=self.pad_offsets,
                                      max_cus=self.max_cus)
         with self._op("fc1_dgrad"):
-            ops.moe_grouped_gemm_bwd(self.dH_row, self.offsets, mode="dgrad", w=W.w1t,
-                                     out=self.dXp, E=E, K=d, max_cus=self.max_cus)
+            if self.mx_dxp:
+                ops.moe_grouped_gemm_bwd(self.dH_row, self.offsets, mode="dgrad", w=W.w1t,
+                                         out_mx=self.dXp, E=E, K=d, max_cus=self.max_cus)
+            else:
+                ops.moe_grouped_gemm_bwd(self.dH_row, self.offsets, mode="dgrad", w=W.w1t,
+                                         out=self.dXp, E=E, K=d, max_cus=self.max_cus)
         with self._op("fc1_wgrad"):
             ops.moe_grouped_gemm_bwd(self.dH_col, self.offsets, mode="wgrad", a=self.xp_col,
                                      out=self.dW1p, E=E, R=R, pad_offsets=self.pad_offsets,
                                      max_cus=self.max_cus)
         with self._op("unpermute_dx"):
-            ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
+            if self.mx_dxp:
+                ops.moe_unpermute_combine_mx(self.dXp, self.row_map, None, out=self.dX)
+            else:
+                ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
         return self.dX
 
     def step(self, x, logits, W1p, W2, d_out, b1p=None, b2=None):

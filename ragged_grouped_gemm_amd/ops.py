@@ -249,17 +249,21 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
     return a_out, (h_out if save_h else None)
 
 
-def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0, E=None, N=None):
-    """y[r] = a[r] @ w[e]^T (+ b[e]).  MXFP8 operands (a, w MXTensor row copies
-    along K; E and N given): y is bf16."""
+def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0, E=None, N=None,
+                         y_mx: Optional[MXTensor] = None):
+    """y[r] = a[r] @ w[e]^T (+ b[e]).  MX operands (a, w MXTensor row copies
+    along K; E and N given): y is bf16, or, with ``y_mx``, an MX row copy in
+    the operands' format (returned instead)."""
     if isinstance(a, MXTensor):
         R, K = a.rows, a.ld
-        y = torch.empty((R, N), dtype=torch.bfloat16, device=a.data.device) if y is None else y
+        if y_mx is None and y is None:
+            y = torch.empty((R, N), dtype=torch.bfloat16, device=a.data.device)
         args = _lib.GemmFwdArgs(ctypes.sizeof(_lib.GemmFwdArgs), a.dtype_code, None, None, None,
-                                _p(offsets), E, R, N, K, _p(y), max_cus, _mx(a), _mx(w))
+                                _p(offsets), E, R, N, K, _p(y), max_cus, _mx(a), _mx(w),
+                                _mx(y_mx))
         check(_lib.load().moe_grouped_gemm_fwd(ctypes.byref(args), _stream()),
               "moe_grouped_gemm_fwd")
-        return y
+        return y if y_mx is None else y_mx
     R, K = a.shape
     E, N, _ = w.shape
     y = _empty((R, N), a.dtype, a) if y is None else y
@@ -305,7 +309,7 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
 
 def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None, want_db=False,
                          accumulate=False, max_cus=0, E=None, R=None, N=None, K=None,
-                         pad_offsets=None, a_src_row=None):
+                         pad_offsets=None, a_src_row=None, out_mx: Optional[MXTensor] = None):
     """mode "dgrad": da = g @ w[e];  mode "wgrad": dw[e] = g[seg]^T @ a[seg] (+ db).
 
     a_src_row (wgrad, gather-fused permute): a is the unpermuted [T, K] and
@@ -318,11 +322,13 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
         dev = g.data.device
         if mode == "dgrad":
             R, N = g.rows, g.ld
-            out = torch.empty((R, K), dtype=torch.bfloat16, device=dev) if out is None else out
+            if out_mx is None and out is None:
+                out = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
             m = _lib.MOE_BWD_DGRAD
             args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), g.dtype_code, m, None, None,
                                     None, _p(offsets), E, R, N, K, _p(out), None, 0, max_cus,
                                     _mx(g), None, _mx(w), None)
+            args.out_mx = _mx(out_mx)
         elif mode == "wgrad":
             N, K = g.rows, a.rows
             out = torch.empty((E, N, K), dtype=torch.float32, device=dev) if out is None else out
@@ -334,7 +340,7 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
             raise ValueError(mode)
         check(_lib.load().moe_grouped_gemm_bwd(ctypes.byref(args), _stream()),
               "moe_grouped_gemm_bwd")
-        return out
+        return out if out_mx is None else out_mx
     R, N = g.shape
     if mode == "dgrad":
         E, _, K = w.shape
@@ -366,6 +372,19 @@ def moe_unpermute_combine(y, row_map, topk_w=None, out=None):
     check(_lib.load().moe_unpermute_combine(_p(y), _dtype(y), _p(row_map), _p(topk_w), T, k, d,
                                             _p(out), _stream()),
           "moe_unpermute_combine")
+    return out
+
+
+def moe_unpermute_combine_mx(y_mx: MXTensor, row_map, topk_w=None, out=None,
+                             out_dtype=torch.bfloat16):
+    """out[t] = sum_j w[t,j] * decode(y_mx)[row_map[t,j]] (float32 sum, one rounding)."""
+    T, k = row_map.shape
+    d = y_mx.ld
+    out = torch.empty((T, d), dtype=out_dtype, device=row_map.device) if out is None else out
+    check(_lib.load().moe_unpermute_combine_mx(_mx(y_mx), y_mx.dtype_code, _p(row_map),
+                                               _p(topk_w), T, k, d, _p(out), _dtype(out),
+                                               _stream()),
+          "moe_unpermute_combine_mx")
     return out
 
 
