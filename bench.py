@@ -50,6 +50,12 @@ def parse():
     ap.add_argument("--recompute", action="store_true",
                     help="bf16 / fp32 training workloads: H is not kept from the forward, the "
                          "backward runs FC1 + GLU again (its FLOP are not counted in the metric)")
+    ap.add_argument("--no-transpose-w2", action="store_true",
+                    help="bf16 / fp32 training workloads: FC2's dgrad reads W2 as stored "
+                         "(MN-contiguous) instead of a transposed copy made in each backward")
+    ap.add_argument("--transpose-w1", action="store_true",
+                    help="bf16 / fp32 training workloads: FC1's dgrad reads a transposed copy "
+                         "of W1p made in each backward")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -88,6 +94,8 @@ def hbm_bytes(cfg, fused_permute=False):
     if cfg.backward:
         if cfg.gemm in ("mxfp8", "mxfp4"):
             out["quantize_dy"] = R * d * b + 2 * mxb(d) + 8 * R
+        f, n1 = cfg.f, cfg.n1
+        out.update({"transpose_w2": 2 * E * d * f * b, "transpose_w1p": 2 * E * d * n1 * b})
         out.update({"combine_bwd": T * d * b + 2 * R * d * b + 12 * R,
                     "route_topk_bwd": T * E * 8 + T * k * 8,
                     "unpermute_dx": R * d * b + T * d * b + 4 * R})
@@ -194,7 +202,8 @@ def main():
     L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
-               recompute=args.recompute, mx_dxp=args.mx_dxp)
+               recompute=args.recompute, mx_dxp=args.mx_dxp,
+               transpose_w2=not args.no_transpose_w2, transpose_w1=args.transpose_w1)
     permute = "fused" if L.fuse_permute else "copy"
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
@@ -269,6 +278,9 @@ def main():
                    "permute": "mx_quantize_gather" if mx else permute,
                    "recompute_fc1": bool(args.recompute),
                    "mx_dxp": bool(args.mx_dxp),
+                   "dgrad_weights_transposed": [n for n, on in
+                                                (("W2", not args.no_transpose_w2 and not mx),
+                                                 ("W1p", args.transpose_w1 and not mx)) if on],
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "gemm_only_tflops": round(total_flops / gemm_ms / 1e9, 2),

@@ -167,6 +167,18 @@ moe_status_t moe_repack_glu_weights(const void* w, const float* b, int dtype, in
                                     int d, int inverse, void* w_out, float* b_out,
                                     void* stream);
 
+/* Transposed copy of per-expert weights for the dgrad GEMMs:
+ * wt[e][j][i] = w[e][i][j].  The backward products dA = dY W2[e] (FC2) and
+ * dXp = dH W1p[e] (FC1) reduce over the rows of the stored weight; with the
+ * transposed copy both of their operands are contiguous along the reduction,
+ * like the forward GEMMs' (moe_glu_bwd_args_t.w2t, moe_gemm_bwd_args_t.wt).
+ * Made once per weight update (the weights do not change within a step).
+ *   w  [E, rows, cols] dtype (in), wt [E, cols, rows] dtype (out, must not
+ *   alias w); rows and cols multiples of 8; 16-byte aligned pointers.
+ * A bit-exact copy; MOE_ERR_INVALID_ARG on bad sizes or pointers. */
+moe_status_t moe_transpose_weights(const void* w, int dtype, int E, int rows, int cols, void* wt,
+                                   void* stream);
+
 /* ---------------------------------------------------------------- grouped GEMMs
  * All grouped GEMMs run over the expert segments given by the DEVICE array
  * offsets [E+1] (offsets[0] = 0, nondecreasing, offsets[E] = R); segment e
@@ -278,6 +290,10 @@ typedef struct {
   moe_mx_t* dh_row;
   moe_mx_t* dh_col;
   const int32_t* pad_offsets;
+  /* bf16 / float32 (nullable): W2 transposed, w2t [E, f, d] with
+   * w2t[e][j][i] == w2[e][i][j] (moe_transpose_weights).  When set it is read
+   * instead of w2 (which may then be NULL), K-contiguous like dy. */
+  const void* w2t;
 } moe_glu_bwd_args_t;
 moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* args, void* stream);
 
@@ -322,6 +338,10 @@ typedef struct {
    * dispatch backward (moe_unpermute_combine_mx sums it); out may then be
    * NULL. */
   moe_mx_t* out_mx;
+  /* DGRAD, bf16 / float32 (nullable): w transposed, wt [E, K, N] with
+   * wt[e][j][i] == w[e][i][j] (moe_transpose_weights).  When set it is read
+   * instead of w (which may then be NULL), K-contiguous like g. */
+  const void* wt;
 } moe_gemm_bwd_args_t;
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream);
 

@@ -54,7 +54,7 @@ class GluBwdArgs(ctypes.Structure):
                 ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
                 ("alpha", c_float), ("gelu_tanh", c_int), ("dh", c_void_p),
                 ("max_cus", c_int), ("dy_mx", _PMX), ("w2t_mx", _PMX), ("dh_row", _PMX),
-                ("dh_col", _PMX), ("pad_offsets", c_void_p)]
+                ("dh_col", _PMX), ("pad_offsets", c_void_p), ("w2t", c_void_p)]
 
 
 class GemmBwdArgs(ctypes.Structure):
@@ -63,7 +63,7 @@ class GemmBwdArgs(ctypes.Structure):
                 ("R", c_int), ("N", c_int), ("K", c_int), ("out", c_void_p), ("db", c_void_p),
                 ("accumulate", c_int), ("max_cus", c_int), ("g_mx", _PMX), ("a_mx", _PMX),
                 ("w_mx", _PMX), ("pad_offsets", c_void_p), ("a_src_row", c_void_p),
-                ("a_src_rows", c_int), ("out_mx", _PMX)]
+                ("a_src_rows", c_int), ("out_mx", _PMX), ("wt", c_void_p)]
 
 
 _SIGS = {
@@ -80,6 +80,7 @@ _SIGS = {
                             c_void_p, c_void_p]),
     "moe_repack_glu_weights": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                        c_void_p, c_void_p, c_void_p]),
+    "moe_transpose_weights": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),
     "moe_grouped_gemm_glu_fwd": (c_int, [ctypes.POINTER(GluFwdArgs), c_void_p]),
     "moe_grouped_gemm_fwd": (c_int, [ctypes.POINTER(GemmFwdArgs), c_void_p]),
     "moe_grouped_gemm_glu_bwd": (c_int, [ctypes.POINTER(GluBwdArgs), c_void_p]),

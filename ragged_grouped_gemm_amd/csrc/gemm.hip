@@ -120,6 +120,7 @@ struct GemmArgs {
   int act, gelu_tanh;
   int accumulate;
   int gm;  // M-tiles per band of the tile order
+  int snake;  // RAGGED_K: odd rounds of the tile order run backwards
   // Gather-fused permute (nullable): RAGGED_M reads row r of A as row
   // gather[r] of a; RAGGED_K reads k-row r of B as row gather[r] of b; the
   // gathered source has gather_rows rows.
@@ -1144,7 +1145,15 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       }
   };
 
-  for (int tile = vb; tile < total; tile += G) {
+  // Round r gives block vb the tile r G + vb.  Weight-gradient tiles are
+  // ordered by decreasing k length (experts largest first), so there odd
+  // rounds run backwards (r G + G - 1 - vb): a block that took one of the
+  // longest tiles of a round takes one of the shortest of the next, which
+  // evens out the per-block sums.  Either way the 32 blocks of an XCD take 32
+  // consecutive tiles of a round.
+  for (int round = 0;; ++round) {
+    const int tile = round * G + ((GROUP == RAGGED_K && p.snake && (round & 1)) ? G - 1 - vb : vb);
+    if (tile >= total) break;
     const TileC cur = decode(tile);
     const int nk = nk_of(cur);
     __syncthreads();  // every wave is done with the previous tile's buffers
@@ -1633,16 +1642,19 @@ moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipSt
   return dispatch_tiles<F32, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
 }
 
-// MOE_GEMM_GM in the environment overrides the band height (for tuning).
+// MOE_GEMM_GM in the environment overrides the band height, MOE_GEMM_SNAKE=0
+// turns the weight gradients' alternating tile order off (for tuning).
 inline GemmArgs zero_args() {
   GemmArgs p;
   memset(&p, 0, sizeof(p));
   p.alpha = 1.0f;
-  p.gm = 8;
+  p.gm = 4;
   if (const char* v = getenv("MOE_GEMM_GM")) {
     int g = atoi(v);
     if (g >= 1 && g <= 64) p.gm = g;
   }
+  p.snake = 1;
+  if (const char* v = getenv("MOE_GEMM_SNAKE")) p.snake = atoi(v) != 0;
   return p;
 }
 
@@ -1675,6 +1687,14 @@ inline const int32_t* gather_field(const A* a, const int32_t* const A::*f) {
   const size_t end = (size_t)(reinterpret_cast<const char*>(&(a->*f)) -
                               reinterpret_cast<const char*>(a)) + sizeof(const int32_t*) +
                      sizeof(int);
+  return a->struct_size >= end ? a->*f : nullptr;
+}
+// An optional pointer field of an argument struct, or NULL when the caller's
+// struct predates it.
+template <class A>
+inline const void* ptr_field(const A* a, const void* const A::*f) {
+  const size_t end = (size_t)(reinterpret_cast<const char*>(&(a->*f)) -
+                              reinterpret_cast<const char*>(a)) + sizeof(const void*);
   return a->struct_size >= end ? a->*f : nullptr;
 }
 // A gathered source [rows, cols] must be addressable by 31-bit byte offsets.
@@ -1950,8 +1970,10 @@ moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream)
   if (a->dtype == MOE_E4M3 || a->dtype == MOE_E2M1)
     return glu_bwd_mx(a, reinterpret_cast<hipStream_t>(stream));
   if (a->R == 0) return MOE_OK;
-  MOE_CHECK_ARG(a->dy && a->w2 && a->h && a->offsets && a->dh);
-  MOE_CHECK_ARG(aligned16(a->dy) && aligned16(a->w2) && aligned16(a->h) && aligned16(a->dh));
+  const void* w2t = ptr_field(a, &moe_glu_bwd_args_t::w2t);
+  MOE_CHECK_ARG(a->dy && (a->w2 || w2t) && a->h && a->offsets && a->dh);
+  MOE_CHECK_ARG(aligned16(a->dy) && aligned16(w2t ? w2t : a->w2) && aligned16(a->h) &&
+                aligned16(a->dh));
   const bool gated = a->act != MOE_ACT_SRELU;
   const int n1 = gated ? 2 * a->f : a->f;
   GemmArgs p = zero_args();
@@ -1975,6 +1997,15 @@ moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream)
   p.gelu_tanh = a->gelu_tanh;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool big = big_ragged_m(a->R, a->E, a->f);
+  if (w2t) {
+    p.b = w2t;        // [E][f][d]: N = f rows, K = d contiguous
+    p.ldb = a->d;
+    if (a->act == MOE_ACT_SWIGLU)
+      return dispatch<true, true, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+    if (a->act == MOE_ACT_GEGLU)
+      return dispatch<true, true, RAGGED_M, EPI_GEGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+    return dispatch<true, true, RAGGED_M, EPI_SRELU_BWD>(a->dtype, p, big, a->max_cus, s);
+  }
   if (a->act == MOE_ACT_SWIGLU)
     return dispatch<true, false, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
   if (a->act == MOE_ACT_GEGLU)
@@ -2001,7 +2032,8 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
   if (a->mode == MOE_BWD_DGRAD) {
     MOE_CHECK_ARG(!gather_field(a, &moe_gemm_bwd_args_t::a_src_row));
     if (a->R == 0) return MOE_OK;
-    MOE_CHECK_ARG(a->w && aligned16(a->w));
+    const void* wt = ptr_field(a, &moe_gemm_bwd_args_t::wt);
+    MOE_CHECK_ARG((a->w || wt) && aligned16(wt ? wt : a->w));
     // da [R, K] = g [R, N] @ w[e] [N, K]:  GEMM M = rows, N' = K, K' = N
     p.a = a->g;
     p.b = a->w;
@@ -2012,6 +2044,13 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
     p.b_expert_stride = (long long)a->N * a->K;
     p.c = a->out;
     p.ldc = a->K;
+    if (wt) {
+      p.b = wt;       // [E][K][N]: N' = K rows, K' = N contiguous
+      p.ldb = a->N;
+      return dispatch<true, true, RAGGED_M, EPI_STORE>(a->dtype, p,
+                                                       big_ragged_m(a->R, a->E, a->K),
+                                                       a->max_cus, s);
+    }
     return dispatch<true, false, RAGGED_M, EPI_STORE>(a->dtype, p,
                                                       big_ragged_m(a->R, a->E, a->K),
                                                       a->max_cus, s);

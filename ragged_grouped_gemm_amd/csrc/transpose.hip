@@ -1,0 +1,95 @@
+// Transposed copy of per-expert weights, w [E, rows, cols] -> wt [E, cols, rows].
+//
+// The dgrad products of the backward pass (dA = dY W2[e] for FC2, dXp =
+// dH W1p[e] for FC1 -- [P1] "融合された GEMM エピローグ…": the backward GEMM
+// whose epilogue applies dGLU) reduce over the rows of the stored weight.
+// With this copy, made once per weight update, the grouped GEMM reads both
+// operands contiguous along the reduction, as in the forward pass.
+//
+// HBM-bound: each element is read and written once.  A lane moves one V x V
+// block (V elements per 16 bytes): V 16-byte loads from consecutive rows, a
+// transpose in registers, V 16-byte stores.  Eight consecutive lanes read
+// 128 contiguous bytes of a source row, and lanes eight apart write 128
+// contiguous bytes of an output row, so every wave access is whole cache
+// lines; a wave covers an 8V x 8V tile, a block four tiles side by side.
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+template <typename S>
+struct TrBlock;
+
+template <>
+struct TrBlock<uint16_t> {  // 8 x 8 bf16: out[j] gathers element j of in[0..7]
+  static constexpr int V = 8;
+  __device__ __forceinline__ static void run(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a = in[2 * w][j >> 1], b = in[2 * w + 1][j >> 1];
+        out[j][w] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+  }
+};
+
+template <>
+struct TrBlock<float> {  // 4 x 4 float32
+  static constexpr int V = 4;
+  __device__ __forceinline__ static void run(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[j][q] = in[q][j];
+  }
+};
+
+template <typename S>
+__global__ void __launch_bounds__(256) transpose_kernel(const S* __restrict__ w, S* __restrict__ wt,
+                                                        int rows, int cols) {
+  constexpr int V = TrBlock<S>::V;
+  constexpr int TW = 8 * V;  // wave tile edge
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.y * TW + (lane >> 3) * V;
+  const int c = (blockIdx.x * 4 + wave) * TW + (lane & 7) * V;
+  if (r >= rows || c >= cols) return;  // rows, cols multiples of 8: blocks are whole
+  const size_t plane = (size_t)blockIdx.z * rows * cols;
+  const S* src = w + plane + (size_t)r * cols + c;
+  S* dst = wt + plane + (size_t)c * rows + r;
+  u32x4 in[V], out[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) in[q] = *reinterpret_cast<const u32x4*>(src + (size_t)q * cols);
+  TrBlock<S>::run(in, out);
+#pragma unroll
+  for (int q = 0; q < V; ++q) *reinterpret_cast<u32x4*>(dst + (size_t)q * rows) = out[q];
+}
+
+}  // namespace
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status_t moe_transpose_weights(const void* w, int dtype, int E, int rows, int cols,
+                                              void* wt, void* stream) {
+  MOE_CHECK_ARG(valid_dtype(dtype));
+  MOE_CHECK_ARG(E >= 1 && rows > 0 && cols > 0 && rows % 8 == 0 && cols % 8 == 0);
+  MOE_CHECK_ARG(w && wt && w != wt && aligned16(w) && aligned16(wt));
+  const size_t bytes = (size_t)E * rows * cols * dtype_size(dtype);
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(wt);
+  MOE_CHECK_ARG(a + bytes <= b || b + bytes <= a);
+  MOE_CHECK_ARG(E <= 65535);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int tw = dtype == MOE_BF16 ? 64 : 32;
+  dim3 grid((cols + 4 * tw - 1) / (4 * tw), (rows + tw - 1) / tw, E);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(w), static_cast<uint16_t*>(wt), rows, cols);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(w), static_cast<float*>(wt), rows, cols);
+  return launch_status();
+}

@@ -16,6 +16,12 @@ permuted copy Xp is never written; FC1 and FC1's weight gradient read each row
 of x through src_row, so the forward keeps a reference to x for the backward
 (x must not change in between).  ``fuse_permute=False`` materializes Xp.
 
+Transposed weights for the dgrads (``transpose_w2``, default on;
+``transpose_w1``): at the start of each backward W2 (and W1p) are copied
+transposed (``moe_transpose_weights``), so FC2's dgrad + dGLU (and FC1's
+dgrad) read both operands contiguous along the reduction; the results are
+bit-identical to reading the weights as stored.
+
 Activation recomputation (``recompute=True``): the forward does not write
 the pre-activation H; the backward first runs FC1 + GLU again (from x or Xp,
 and the routing the forward left in place) to rebuild H and A, then proceeds
@@ -60,7 +66,7 @@ class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
-                 recompute=False, mx_dxp=False):
+                 recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
             raise ValueError(gemm)
@@ -117,6 +123,9 @@ class MoEFFN:
             self.dW2 = z((E, d, f), f32)
             self.db1p = z((E, n1), f32) if bias else None
             self.db2 = z((E, d), f32) if bias else None
+            # transposed weight copies for the dgrad GEMMs, refreshed every backward
+            self.W2t = z((E, f, d), dtype) if transpose_w2 else None
+            self.W1pt = z((E, d, n1), dtype) if transpose_w1 else None
 
     def _alloc_mx(self, z, dev):
         T, d, f, E, R, n1 = self.T, self.d, self.f, self.E, self.R, self.n1
@@ -201,17 +210,24 @@ class MoEFFN:
         with self._op("route_topk_bwd"):
             ops.moe_route_topk_bwd(logits, self.topk_idx, self.dgate, self.score,
                                    self.normalize, d_logits=self.dlogits)
+        if self.W2t is not None:
+            with self._op("transpose_w2"):
+                ops.moe_transpose_weights(W2, self.W2t)
         with self._op("fc2_dgrad_dglu"):
-            ops.moe_grouped_gemm_glu_bwd(self.dY, W2, self.H, self.offsets, act=self.act,
-                                         clamp=self.clamp, alpha=self.alpha,
-                                         gelu_tanh=self.gelu_tanh, dh=self.dH,
-                                         max_cus=self.max_cus)
+            ops.moe_grouped_gemm_glu_bwd(self.dY, None if self.W2t is not None else W2, self.H,
+                                         self.offsets, act=self.act, clamp=self.clamp,
+                                         alpha=self.alpha, gelu_tanh=self.gelu_tanh, dh=self.dH,
+                                         max_cus=self.max_cus, w2t=self.W2t)
         with self._op("fc2_wgrad"):
             ops.moe_grouped_gemm_bwd(self.dY, self.offsets, mode="wgrad", a=self.A, out=self.dW2,
                                      db=self.db2, max_cus=self.max_cus)
+        if self.W1pt is not None:
+            with self._op("transpose_w1p"):
+                ops.moe_transpose_weights(W1p, self.W1pt)
         with self._op("fc1_dgrad"):
-            ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="dgrad", w=W1p, out=self.dXp,
-                                     max_cus=self.max_cus)
+            ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="dgrad",
+                                     w=None if self.W1pt is not None else W1p, out=self.dXp,
+                                     max_cus=self.max_cus, wt=self.W1pt)
         with self._op("fc1_wgrad"):
             if self.fuse_permute:
                 ops.moe_grouped_gemm_bwd(self.dH, self.offsets, mode="wgrad", a=self.x_saved,

@@ -202,6 +202,15 @@ def moe_repack_glu_weights(w, b=None, inverse=False, w_out=None, b_out=None):
     return w_out, b_out
 
 
+def moe_transpose_weights(w, wt=None):
+    """wt [E, cols, rows] with wt[e][j][i] = w[e][i][j] (w [E, rows, cols])."""
+    E, rows, cols = w.shape
+    wt = torch.empty((E, cols, rows), dtype=w.dtype, device=w.device) if wt is None else wt
+    check(_lib.load().moe_transpose_weights(_p(w), _dtype(w), E, rows, cols, _p(wt), _stream()),
+          "moe_transpose_weights")
+    return wt
+
+
 def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=0.0, alpha=1.0,
                              gelu_tanh=False, save_h=True, h_out=None, a_out=None, max_cus=0,
                              E=None, f=None, pad_offsets=None, a_row=None, a_col=None,
@@ -275,8 +284,11 @@ def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0, E=None, N=
 
 def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alpha=1.0,
                              gelu_tanh=False, dh=None, max_cus=0, E=None, pad_offsets=None,
-                             dh_row=None, dh_col=None, want_row=True, want_col=True):
+                             dh_row=None, dh_col=None, want_row=True, want_col=True, w2t=None):
     """FC2 dgrad + dGLU epilogue -> dH [R, n1] (packed like h).
+
+    w2t (bf16 / fp32, optional): W2 transposed [E, f, d] (moe_transpose_weights),
+    read instead of w2 (which may then be None).
 
     MXFP8 operands (dy row copy along d, w2 the transposed copy [E*f, d]; E
     given; h bf16): returns (dH row copy, dH column copy)."""
@@ -297,11 +309,15 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
               "moe_grouped_gemm_glu_bwd")
         return (dh_row if want_row else None), (dh_col if want_col else None)
     R, d = dy.shape
-    E, _, f = w2.shape
+    if w2t is not None:
+        E, f, _ = w2t.shape
+    else:
+        E, _, f = w2.shape
     dh = torch.empty_like(h) if dh is None else dh
     args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), _dtype(dy), _p(dy), _p(w2), _p(h),
                            _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                            _p(dh), max_cus)
+    args.w2t = _p(w2t)
     check(_lib.load().moe_grouped_gemm_glu_bwd(ctypes.byref(args), _stream()),
           "moe_grouped_gemm_glu_bwd")
     return dh
@@ -309,8 +325,12 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
 
 def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None, want_db=False,
                          accumulate=False, max_cus=0, E=None, R=None, N=None, K=None,
-                         pad_offsets=None, a_src_row=None, out_mx: Optional[MXTensor] = None):
+                         pad_offsets=None, a_src_row=None, out_mx: Optional[MXTensor] = None,
+                         wt=None):
     """mode "dgrad": da = g @ w[e];  mode "wgrad": dw[e] = g[seg]^T @ a[seg] (+ db).
+
+    wt (dgrad, bf16 / fp32, optional): w transposed [E, K, N]
+    (moe_transpose_weights), read instead of w (which may then be None).
 
     a_src_row (wgrad, gather-fused permute): a is the unpermuted [T, K] and
     row r of the segments reads a[a_src_row[r]].
@@ -343,7 +363,10 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
         return out if out_mx is None else out_mx
     R, N = g.shape
     if mode == "dgrad":
-        E, _, K = w.shape
+        if wt is not None:
+            E, K, _ = wt.shape
+        else:
+            E, _, K = w.shape
         out = _empty((R, K), g.dtype, g) if out is None else out
         m = _lib.MOE_BWD_DGRAD
     elif mode == "wgrad":
@@ -357,6 +380,7 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
         raise ValueError(mode)
     args = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), _dtype(g), m, _p(g), _p(a), _p(w),
                             _p(offsets), E, R, N, K, _p(out), _p(db), int(accumulate), max_cus)
+    args.wt = _p(wt)
     if a_src_row is not None:
         args.a_src_row = _p(a_src_row)
         args.a_src_rows = a.shape[0]

@@ -66,12 +66,13 @@ def _device_inputs(cfg, inp):
     return x, lg, W1p, W2, b1p, b2, dout
 
 
-def _layer(cfg, fused=False, recompute=False):
+def _layer(cfg, fused=False, recompute=False, transpose_w2=True, transpose_w1=False):
     from ragged_grouped_gemm_amd.layer import MoEFFN
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     return MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
                   normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-                  backward=cfg.backward, fuse_permute=fused, recompute=recompute)
+                  backward=cfg.backward, fuse_permute=fused, recompute=recompute,
+                  transpose_w2=transpose_w2, transpose_w1=transpose_w1)
 
 
 def _oracle(cfg, inp):
@@ -197,6 +198,28 @@ def test_fused_gather_layer_is_bit_identical(name):
              "dgate", "dlogits", "dW1p", "dW2"] + (["db1p", "db2"] if cfg.bias else [])
     for n in names:
         assert torch.equal(getattr(outs[0], n), getattr(outs[1], n)), n
+
+
+@pytest.mark.parametrize("name", ["dsv3_small", "mixtral_bigtile", "fp32_gated_clamp",
+                                  "srelu_small"])
+def test_transposed_dgrad_weights_are_bit_identical(name):
+    """The dgrads reading transposed weight copies (W2 for FC2 + dGLU, W1p
+    for FC1) give exactly the gradients of the dgrads reading the weights as
+    stored: the same products summed in the same order."""
+    cfg = CASES[name]
+    note(f"transposed vs stored dgrad weights {name}")
+    inp = synth.make_inputs(cfg)
+    x, lg, W1p, W2, b1p, b2, dout = _device_inputs(cfg, inp)
+    Ls = [_layer(cfg, True, transpose_w2=t2, transpose_w1=t1)
+          for t2, t1 in ((False, False), (True, False), (True, True))]
+    for L in Ls:
+        L.forward(x, lg, W1p, W2, b1p, b2)
+        L.backward(dout, lg, W1p, W2)
+    torch.cuda.synchronize()
+    names = ["dH", "dXp", "dX", "dlogits", "dW1p", "dW2"] + (["db1p", "db2"] if cfg.bias else [])
+    for L in Ls[1:]:
+        for n in names:
+            assert torch.equal(getattr(Ls[0], n), getattr(L, n)), n
 
 
 @pytest.mark.parametrize("name,fused", [("dsv3_small", True), ("dsv3_small", False),

@@ -148,6 +148,18 @@ def test_repack_roundtrip(dtype):
     np.testing.assert_array_equal(host(bb), bh)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("E,rows,cols", [(3, 72, 200), (2, 64, 64), (5, 2880, 136)])
+def test_transpose_weights(dtype, E, rows, cols):
+    note(f"transpose_weights {dtype} E={E} {rows}x{cols}")
+    rng = np.random.default_rng(rows + cols)
+    mk = rand_bf16 if dtype == "bf16" else rand_f32
+    wh, wd = mk(rng, (E, rows, cols))
+    wt = ops.moe_transpose_weights(wd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(wt), wh.transpose(0, 2, 1))   # a bit-exact copy
+
+
 # ------------------------------------------------------------------ grouped GEMMs
 
 def _setup(counts, seed):
@@ -246,7 +258,11 @@ def test_glu_bwd(dtype, counts, d, f, act, clamp):
     w2h, w2d = mk(rng, (E, d, f), d ** -0.5)
     hh, hd = mk(rng, (R, n1))          # saved pre-activation, packed layout
     dh = ops.moe_grouped_gemm_glu_bwd(dyd, w2d, hd, offd, act=act, clamp=clamp)
+    # W2 transposed (both operands K-contiguous): the same products in the same order
+    dh_t = ops.moe_grouped_gemm_glu_bwd(dyd, None, hd, offd, act=act, clamp=clamp,
+                                        w2t=ops.moe_transpose_weights(w2d))
     torch.cuda.synchronize()
+    assert torch.equal(dh, dh_t)
     dA = om.grouped_dgrad(dyh, w2h, off)
     if act == "srelu":
         ref = om.srelu_backward(dA, hh, clamp)
@@ -271,7 +287,9 @@ def test_gemm_dgrad(dtype, counts, N, K):
     gh, gd = mk(rng, (R, N))
     wh, wd = mk(rng, (E, N, K), N ** -0.5)
     da = ops.moe_grouped_gemm_bwd(gd, offd, mode="dgrad", w=wd)
+    da_t = ops.moe_grouped_gemm_bwd(gd, offd, mode="dgrad", wt=ops.moe_transpose_weights(wd))
     torch.cuda.synchronize()
+    assert torch.equal(da, da_t)
     ref = om.grouped_dgrad(gh, wh, off)
     if dtype == "bf16":
         assert bf16_excess(host(da), ref) <= TOL_BF16 / 4
