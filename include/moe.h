@@ -386,6 +386,14 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* args, void* stream)
  * R + 31 E rounded up to a multiple of 128 (an upper bound of pad_offsets[E]). */
 int64_t moe_mx_col_len(int R, int E);
 
+/* Leading dimension to allocate a column copy with (elements, >= the
+ * length above): the smallest one whose row stride in bytes is an odd
+ * multiple of 128 (dtype MOE_E4M3 or MOE_E2M1; 0 for another dtype).  The
+ * weight-gradient GEMMs read 128 bytes of many rows at once; with a row
+ * stride of an even multiple of 128 bytes (the length above at most
+ * workload shapes) those reads fall on few HBM channels and run slower. */
+int64_t moe_mx_col_ld(int R, int E, int dtype);
+
 /* Row copy: out = MX(x) along the last axis.  x [rows, n] dtype (F32 or BF16),
  * n a multiple of 32; out->data [rows, out->ld >= n], blocks along n. */
 moe_status_t moe_mx_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,

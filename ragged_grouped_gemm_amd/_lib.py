@@ -90,6 +90,7 @@ _SIGS = {
     "moe_unpermute_combine_bwd": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_int,
                                           c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "moe_mx_col_len": (ctypes.c_int64, [c_int, c_int]),
+    "moe_mx_col_ld": (ctypes.c_int64, [c_int, c_int, c_int]),
     "moe_mx_quantize": (c_int, [c_void_p, c_int, ctypes.c_int64, c_int, _PMX, c_void_p]),
     "moe_mx_quantize_transpose": (c_int, [c_void_p, c_int, c_int, c_int, c_int, _PMX, c_void_p]),
     "moe_mx_quantize_experts": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int,

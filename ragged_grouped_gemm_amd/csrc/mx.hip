@@ -430,6 +430,14 @@ int64_t moe_mx_col_len(int R, int E) {
   return (n + 127) / 128 * 128;
 }
 
+int64_t moe_mx_col_ld(int R, int E, int dtype) {
+  if (dtype != MOE_E4M3 && dtype != MOE_E2M1) return 0;
+  const int64_t unit = dtype == MOE_E2M1 ? 256 : 128;  // elements per 128 bytes
+  int64_t lines = (moe_mx_col_len(R, E) + unit - 1) / unit;
+  if (lines % 2 == 0) ++lines;
+  return lines * unit;
+}
+
 moe_status_t moe_mx_quantize(const void* x, int dtype, int64_t rows, int n, moe_mx_t* out,
                              void* stream) {
   return mx_quantize_impl<FmtE4M3>(x, dtype, rows, n, out, stream);

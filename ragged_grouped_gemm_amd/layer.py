@@ -129,7 +129,7 @@ class MoEFFN:
 
     def _alloc_mx(self, z, dev):
         T, d, f, E, R, n1 = self.T, self.d, self.f, self.E, self.R, self.n1
-        L = ops.moe_mx_col_len(R, E)
+        L = ops.moe_mx_col_ld(R, E, self.mx_fmt)   # padded row stride of the column copies
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
 
         fmt = self.mx_fmt

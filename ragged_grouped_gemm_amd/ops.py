@@ -80,6 +80,12 @@ def moe_mx_col_len(R: int, E: int) -> int:
     return int(_lib.load().moe_mx_col_len(R, E))
 
 
+def moe_mx_col_ld(R: int, E: int, fmt: str = "e4m3") -> int:
+    """Leading dimension of a column copy: row stride an odd multiple of 128 bytes."""
+    code = _lib.MOE_E2M1 if fmt == "e2m1" else _lib.MOE_E4M3
+    return int(_lib.load().moe_mx_col_ld(R, E, code))
+
+
 def _qname(base, fmt):
     return base.replace("moe_mx_", "moe_mxfp4_") if fmt == "e2m1" else base
 
@@ -114,7 +120,7 @@ def moe_mx_quantize_experts(x, offsets, pad_offsets, R, *, src_row=None, row_map
     if want_row and row_out is None:
         row_out = MXTensor(R, n, x.device, fmt=fmt)
     if want_col and col_out is None:
-        col_out = MXTensor(n, moe_mx_col_len(R, E), x.device, fmt=fmt)
+        col_out = MXTensor(n, moe_mx_col_ld(R, E, fmt), x.device, fmt=fmt)
     fmt = (row_out if want_row else col_out).fmt
     name = _qname("moe_mx_quantize_experts", fmt)
     check(getattr(_lib.load(), name)(
@@ -228,7 +234,7 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
         if want_row and a_row is None:
             a_row = MXTensor(R, f, dev, fmt=xp.fmt)
         if want_col and a_col is None:
-            a_col = MXTensor(f, moe_mx_col_len(R, E), dev, fmt=xp.fmt)
+            a_col = MXTensor(f, moe_mx_col_ld(R, E, xp.fmt), dev, fmt=xp.fmt)
         if save_h and h_out is None:
             h_out = torch.empty((R, n1), dtype=torch.bfloat16, device=dev)
         args = _lib.GluFwdArgs(ctypes.sizeof(_lib.GluFwdArgs), xp.dtype_code, None, None, None,
@@ -300,7 +306,7 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
         if want_row and dh_row is None:
             dh_row = MXTensor(R, n1, dev, fmt=dy.fmt)
         if want_col and dh_col is None:
-            dh_col = MXTensor(n1, moe_mx_col_len(R, E), dev, fmt=dy.fmt)
+            dh_col = MXTensor(n1, moe_mx_col_ld(R, E, dy.fmt), dev, fmt=dy.fmt)
         args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), dy.dtype_code, None, None, _p(h),
                                _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                                None, max_cus, _mx(dy), _mx(w2), _mx(dh_row if want_row else None),

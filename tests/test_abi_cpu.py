@@ -71,6 +71,13 @@ def test_mx_host_checks():
     # token axis of a column copy: R + 31 E rounded up to 128
     assert lib.moe_mx_col_len(100, 2) == 256
     assert lib.moe_mx_col_len(131072, 32) == 132096
+    # allocation stride: the smallest ld >= that length whose rows are an odd
+    # number of 128-byte lines (E4M3: 1 byte per element, E2M1: 2 per byte)
+    assert lib.moe_mx_col_ld(131072, 32, _lib.MOE_E4M3) == 1033 * 128
+    assert lib.moe_mx_col_ld(131072, 32, _lib.MOE_E2M1) == 517 * 256
+    assert lib.moe_mx_col_ld(100, 2, _lib.MOE_E4M3) == 384
+    assert lib.moe_mx_col_ld(100, 2, _lib.MOE_E2M1) == 256
+    assert lib.moe_mx_col_ld(100, 2, _lib.MOE_BF16) == 0
     fake = ctypes.c_void_p(256)
     good = _lib.MxT(256, 256, 64)
     # n not a multiple of 32; ld smaller than n; misaligned codes
