@@ -263,6 +263,10 @@ def test_graph_replay_matches_eager_and_is_deterministic(fused):
     for seed in (11, 12, 13):
         new_lg = synth.draw_router(cfg.replace(seed=seed))
         lg.copy_(synth.to_torch(new_lg, "cuda"))
+        if seed == 13:
+            # new weights: the step's transposed weight copies are remade
+            W2.mul_(0.5)
+            W1p.mul_(-1.0)
         graph.replay()
         torch.cuda.synchronize()
         Le.step(x, lg, W1p, W2, dout)
