@@ -844,6 +844,52 @@ __device__ __forceinline__ void glu_fwd_values(uint16_t* __restrict__ Hrow, cons
   }
 }
 
+// The saved H values one lane needs for a 32 x 32 block of dA whose first
+// column (of this lane) is c0: gate and linear bf16 of 4 runs of 4 columns,
+// as raw bits (zeros when Hrow is NULL, i.e. the row is past the segment).
+__device__ __forceinline__ void glu_bwd_hload(const uint16_t* __restrict__ Hrow, int c0,
+                                              u32x2 (&h)[4][2]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int col = c0 + 8 * g;
+    const int pg = (col >> 5) * 64 + (col & 31);
+    h[g][0] = Hrow ? *reinterpret_cast<const u32x2*>(Hrow + pg) : u32x2{0u, 0u};
+    h[g][1] = Hrow ? *reinterpret_cast<const u32x2*>(Hrow + pg + 32) : u32x2{0u, 0u};
+  }
+}
+
+// dGLU of one block from its loaded H (glu_bwd_hload); `live` = the row is
+// inside the segment (else the outputs are 0).
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_values_h(const u32x2 (&h)[4][2], bool live,
+                                                 const f32x16& acc, float L, float alpha,
+                                                 int gtanh, float* dg, float* dl) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float hg[4], hl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hg[q] = bf16_bits_to_f32((h[g][0][q >> 1] >> (16 * (q & 1))) & 0xffffu);
+      hl[q] = bf16_bits_to_f32((h[g][1][q >> 1] >> (16 * (q & 1))) & 0xffffu);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float gt = hg[q], li = hl[q], mg = 1.0f, ml = 1.0f;
+      if (L > 0.0f) {
+        mg = gt <= L ? 1.0f : 0.0f;
+        ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
+        gt = fminf(gt, L);
+        li = fminf(fmaxf(li, -L), L);
+      }
+      float a, da_dg;
+      act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
+      const float d = live ? acc[4 * g + q] : 0.0f;
+      dg[4 * g + q] = d * li * da_dg * mg;
+      dl[4 * g + q] = d * a * ml;
+    }
+  }
+}
+
 // dGLU values of one dA block: gate and linear gradients (zero when Hrow is
 // null, i.e. for rows past the segment).
 template <int ACT>
@@ -1403,6 +1449,15 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       const int pe0 = p.pad_offsets ? p.pad_offsets[e] : 0;
       const int pe1 = p.pad_offsets ? p.pad_offsets[e + 1] : 0;
       const int off_e = s_off[e];
+      u32x2 hbuf[2][4][2];  // dGLU: saved H of the current and the next block
+      if constexpr (epi_glu_bwd(EPI)) {
+        const int row0 = m0 + wm * C::WTM + (lane & 31);
+        const int cb0 = n0 + wn * C::WTN;
+        glu_bwd_hload((row0 < mlim && cb0 < p.N)
+                          ? reinterpret_cast<const SO*>(p.aux) + (size_t)row0 * p.ld_aux
+                          : nullptr,
+                      cb0 + 4 * (lane >> 5), hbuf[0]);
+      }
       static_for<0, TM>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         const int r0 = m0 + wm * C::WTM + 32 * i;
@@ -1428,11 +1483,23 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
               }
             }
           } else {
+            // the saved H of the next block (j + 1, or row block i + 1) is
+            // requested before this block is computed and stored, so its load
+            // latency hides behind this block's quantization
+            constexpr int b = i * TN + j;
+            if constexpr (b + 1 < TM * TN) {
+              constexpr int i2 = (b + 1) / TN, j2 = (b + 1) % TN;
+              const int row2 = m0 + wm * C::WTM + 32 * i2 + (lane & 31);
+              const int cb2 = n0 + wn * C::WTN + 32 * j2;
+              glu_bwd_hload((row2 < mlim && cb2 < p.N)
+                                ? reinterpret_cast<const SO*>(p.aux) + (size_t)row2 * p.ld_aux
+                                : nullptr,
+                            cb2 + 4 * (lane >> 5), hbuf[(b + 1) & 1]);
+            }
             if (cb < p.N) {
               float dg[16], dl[16];
-              glu_bwd_values<epi_act(EPI)>(
-                  rok ? reinterpret_cast<const SO*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
-                  acc[i][j], cb + 4 * (lane >> 5), p.clamp, p.alpha, p.gelu_tanh, dg, dl);
+              glu_bwd_values_h<epi_act(EPI)>(hbuf[b & 1], rok, acc[i][j], p.clamp, p.alpha,
+                                             p.gelu_tanh, dg, dl);
               const int pg0 = (cb >> 5) * 64;
               mx_stage(Wt, lane, dg);
               wave_lds_sync();
