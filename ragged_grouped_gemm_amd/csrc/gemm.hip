@@ -17,20 +17,22 @@
 // Design (gfx950 / CDNA4):
 //  * Persistent launch: grid = (compute units) x (resident workgroups per
 //    CU).  Each workgroup reads offsets[E+1] once, builds the tile table in
-//    LDS and walks the tiles tile = vb, vb + grid, ...  The virtual id vb
+//    LDS and takes one tile per round, r * grid + vb.  The virtual id vb
 //    groups consecutive tiles on one XCD (blocks are dealt round-robin over
-//    the 8 XCDs), and tiles are ordered in bands of GM M-tiles so the
-//    workgroups of an XCD share A rows and B columns in its L2.
+//    the 8 XCDs), and tiles are ordered in bands of GM M-tiles (default 4)
+//    so the workgroups of an XCD share A rows and B columns in its L2.
 //  * Two grouping modes: RAGGED_M (FC1, FC2, dgrads: M = rows of an expert,
 //    B = that expert's weight) and RAGGED_K (weight gradients: K = rows of an
-//    expert; experts visited largest first so the long tiles start early).
-//  * Tiles of BM x BN x (128 bytes of K), double-buffered in LDS.  Every LDS
-//    row holds 128 bytes of K as eight 16-byte chunks, chunk c of row r stored
-//    at slot c ^ (r & 7), so a quarter-wave reading eight rows at one chunk
-//    hits all 32 banks.  K-contiguous operands are copied as 16-byte chunks;
-//    MN-contiguous operands (the transposed operands of dgrad / wgrad) are
-//    loaded as VEC x VEC element blocks and transposed in registers before the
-//    LDS store, so the MFMA loop always reads K-contiguous fragments.
+//    expert; experts visited largest first so the long tiles start early,
+//    and odd rounds run backwards to even out the per-block sums).
+//  * Tiles of BM x BN x (128 bytes of K) in a ring of LDS stages, filled by
+//    LDS-DMA loads (buffer_load ... lds, no staging registers).  A
+//    K-contiguous operand keeps 128 bytes of K per LDS row, 16-byte chunk c
+//    of row r at slot c ^ ((r >> 1) & 7), so fragment reads touch every bank
+//    once.  An MN-contiguous operand (the transposed operand of a dgrad or
+//    weight gradient) keeps one k per LDS row and is read with
+//    ds_read_b64_tr_b16, which hands each lane the k-run its MFMA fragment
+//    needs.
 //  * MFMA v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32),
 //    fp32 accumulation.  The MFMA is issued with B as the first operand, so a
 //    lane's 16 accumulators hold 4 runs of 4 consecutive output columns of one
