@@ -64,6 +64,36 @@ def test_bad_arguments_rejected(lib):
     assert lib.moe_grouped_gemm_bwd(ctypes.byref(b), None) == INV
 
 
+def test_transpose_weights_host_checks(lib):
+    """moe_transpose_weights: sizes, pointers and aliasing are checked before
+    anything is launched."""
+    INV = _lib.MOE_ERR_INVALID_ARG
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24)
+    assert lib.moe_transpose_weights(a, 1, 2, 12, 64, b, None) == INV       # rows % 8
+    assert lib.moe_transpose_weights(a, 1, 2, 64, 12, b, None) == INV       # cols % 8
+    assert lib.moe_transpose_weights(a, 1, 0, 64, 64, b, None) == INV       # E
+    assert lib.moe_transpose_weights(a, 5, 2, 64, 64, b, None) == INV       # dtype
+    assert lib.moe_transpose_weights(None, 1, 2, 64, 64, b, None) == INV
+    assert lib.moe_transpose_weights(a, 1, 2, 64, 64, a, None) == INV       # in place
+    # overlapping source and destination
+    assert lib.moe_transpose_weights(a, 1, 2, 64, 64, ctypes.c_void_p((1 << 20) + 4096),
+                                     None) == INV
+    assert lib.moe_transpose_weights(ctypes.c_void_p((1 << 20) + 2), 1, 2, 64, 64, b,
+                                     None) == INV                           # misaligned
+    # the dgrads' transposed operands must be 16-byte aligned too
+    g = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), 1, 256, None, 256, 256, 4, 64, 64, 64,
+                        0, 0.0, 1.0, 0, 256, 0)
+    g.w2t = 258
+    assert lib.moe_grouped_gemm_glu_bwd(ctypes.byref(g), None) == INV
+    g.w2t = None                                                            # neither w2 nor w2t
+    assert lib.moe_grouped_gemm_glu_bwd(ctypes.byref(g), None) == INV
+    d = _lib.GemmBwdArgs(ctypes.sizeof(_lib.GemmBwdArgs), 1, _lib.MOE_BWD_DGRAD, 256, None,
+                         None, 256, 4, 64, 64, 64, 256, None, 0, 0)
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(d), None) == INV          # neither w nor wt
+    d.wt = 264
+    assert lib.moe_grouped_gemm_bwd(ctypes.byref(d), None) == INV
+
+
 def test_mx_host_checks():
     """MXFP8 entry points: host-side sizes and argument errors (nothing is launched)."""
     lib = _lib.load()
