@@ -84,6 +84,7 @@ extern "C" moe_status_t moe_transpose_weights(const void* w, int dtype, int E, i
   MOE_CHECK_ARG(E <= 65535);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int tw = dtype == MOE_BF16 ? 64 : 32;
+  MOE_CHECK_ARG((rows + tw - 1) / tw <= 65535);
   dim3 grid((cols + 4 * tw - 1) / (4 * tw), (rows + tw - 1) / tw, E);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s,

@@ -212,6 +212,8 @@ def moe_transpose_weights(w, wt=None):
     """wt [E, cols, rows] with wt[e][j][i] = w[e][i][j] (w [E, rows, cols])."""
     E, rows, cols = w.shape
     wt = torch.empty((E, cols, rows), dtype=w.dtype, device=w.device) if wt is None else wt
+    if tuple(wt.shape) != (E, cols, rows) or wt.dtype != w.dtype:
+        raise ValueError(f"wt must be {(E, cols, rows)} {w.dtype}, got {tuple(wt.shape)} {wt.dtype}")
     check(_lib.load().moe_transpose_weights(_p(w), _dtype(w), E, rows, cols, _p(wt), _stream()),
           "moe_transpose_weights")
     return wt
@@ -316,9 +318,11 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
         return (dh_row if want_row else None), (dh_col if want_col else None)
     R, d = dy.shape
     if w2t is not None:
-        E, f, _ = w2t.shape
+        E, f, d2 = w2t.shape
     else:
-        E, _, f = w2.shape
+        E, d2, f = w2.shape
+    if d2 != d:
+        raise ValueError(f"the weight's d ({d2}) differs from dy's ({d})")
     dh = torch.empty_like(h) if dh is None else dh
     args = _lib.GluBwdArgs(ctypes.sizeof(_lib.GluBwdArgs), _dtype(dy), _p(dy), _p(w2), _p(h),
                            _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
@@ -370,9 +374,11 @@ def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None,
     R, N = g.shape
     if mode == "dgrad":
         if wt is not None:
-            E, K, _ = wt.shape
+            E, K, N2 = wt.shape
         else:
-            E, _, K = w.shape
+            E, N2, K = w.shape
+        if N2 != N:
+            raise ValueError(f"the weight's N ({N2}) differs from g's ({N})")
         out = _empty((R, K), g.dtype, g) if out is None else out
         m = _lib.MOE_BWD_DGRAD
     elif mode == "wgrad":
