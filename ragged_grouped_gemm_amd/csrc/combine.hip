@@ -74,6 +74,22 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
 // rows of a chunk (and, backward, reads d_out once) before using any, so each
 // lane keeps k + 1 loads in flight.  Sums run in the same order as above, so
 // the results are identical.
+// 16-byte global access, optionally with the nontemporal hint.  The combine
+// and the unpermute-sum stream their inputs (every routed row is read once)
+// and outputs (read by no later kernel of the layer) with it: measured 8 %
+// and 16 % faster at dsv3_fwdbwd.  The combine backward writes dY, which
+// the next GEMMs read, so it keeps the default policy.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(u32x4* p, const u32x4& v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 template <class EL, int K>
 __global__ void __launch_bounds__(256) combine_kernel_k(const u32x4* __restrict__ y,
                                                         const int32_t* __restrict__ row_map,
@@ -94,7 +110,7 @@ __global__ void __launch_bounds__(256) combine_kernel_k(const u32x4* __restrict_
   for (int c = lane; c < chunks; c += 64) {
     u32x4 raw[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) raw[j] = y[(size_t)rows[j] * chunks + c];
+    for (int j = 0; j < K; ++j) raw[j] = ld16<true>(y + (size_t)rows[j] * chunks + c);
     float acc[V];
 #pragma unroll
     for (int q = 0; q < V; ++q) acc[q] = 0.0f;
@@ -105,7 +121,7 @@ __global__ void __launch_bounds__(256) combine_kernel_k(const u32x4* __restrict_
 #pragma unroll
       for (int q = 0; q < V; ++q) acc[q] = fmaf(ws[j], v[q], acc[q]);
     }
-    out[(size_t)t * chunks + c] = pack_chunk(acc, EL());
+    st16<true>(out + (size_t)t * chunks + c, pack_chunk(acc, EL()));
   }
 }
 
