@@ -12,6 +12,8 @@
 // 128 contiguous bytes of a source row, and lanes eight apart write 128
 // contiguous bytes of an output row, so every wave access is whole cache
 // lines; a wave covers an 8V x 8V tile, a block four tiles side by side.
+// Loads and stores carry the nontemporal hint (each byte is touched once):
+// 0.35 -> 0.335 ms for W2 at dsv3_fwdbwd.
 #include "common.hpp"
 
 namespace moe {
@@ -60,10 +62,12 @@ __global__ void __launch_bounds__(256) transpose_kernel(const S* __restrict__ w,
   S* dst = wt + plane + (size_t)c * rows + r;
   u32x4 in[V], out[V];
 #pragma unroll
-  for (int q = 0; q < V; ++q) in[q] = *reinterpret_cast<const u32x4*>(src + (size_t)q * cols);
+  for (int q = 0; q < V; ++q)
+    in[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)q * cols));
   TrBlock<S>::run(in, out);
 #pragma unroll
-  for (int q = 0; q < V; ++q) *reinterpret_cast<u32x4*>(dst + (size_t)q * rows) = out[q];
+  for (int q = 0; q < V; ++q)
+    __builtin_nontemporal_store(out[q], reinterpret_cast<u32x4*>(dst + (size_t)q * rows));
 }
 
 }  // namespace
