@@ -147,8 +147,15 @@ __global__ void __launch_bounds__(256)
   __shared__ float s_w[32];
   __shared__ int s_row[32];                // routed row of tile row i (or -1)
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * 256;
-  for (long long g = blockIdx.y; g < ngroups; g += gridDim.y) {
+  // Workgroups are dealt round-robin over the 8 XCDs in launch order.  The
+  // column copy of group g + 1 continues the 32-byte pieces of group g in the
+  // same rows, so consecutive groups of one column chunk go to one XCD: its
+  // L2 then merges the pieces into whole lines before they reach HBM.
+  const int nb = gridDim.x * gridDim.y, n8 = nb & ~7;
+  int vid = blockIdx.y * gridDim.x + blockIdx.x;
+  if (vid < n8) vid = (vid & 7) * (n8 >> 3) + (vid >> 3);
+  const int c0 = (vid / gridDim.y) * 256;
+  for (long long g = vid % gridDim.y; g < ngroups; g += gridDim.y) {
     const int prow0 = (int)(g * 32);
     if (prow0 >= pad_offsets[E]) break;    // same for the whole workgroup
     int lo = 0, hi = E;                    // largest e with pad_offsets[e] <= prow0
