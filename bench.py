@@ -53,9 +53,9 @@ def parse():
     ap.add_argument("--no-transpose-w2", action="store_true",
                     help="bf16 / fp32 training workloads: FC2's dgrad reads W2 as stored "
                          "(MN-contiguous) instead of a transposed copy made in each backward")
-    ap.add_argument("--transpose-w1", action="store_true",
-                    help="bf16 / fp32 training workloads: FC1's dgrad reads a transposed copy "
-                         "of W1p made in each backward")
+    ap.add_argument("--no-transpose-w1", action="store_true",
+                    help="bf16 / fp32 training workloads: FC1's dgrad reads W1p as stored "
+                         "(MN-contiguous) instead of a transposed copy made in each backward")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -203,7 +203,7 @@ def main():
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
                recompute=args.recompute, mx_dxp=args.mx_dxp,
-               transpose_w2=not args.no_transpose_w2, transpose_w1=args.transpose_w1)
+               transpose_w2=not args.no_transpose_w2, transpose_w1=not args.no_transpose_w1)
     permute = "fused" if L.fuse_permute else "copy"
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
@@ -280,7 +280,8 @@ def main():
                    "mx_dxp": bool(args.mx_dxp),
                    "dgrad_weights_transposed": [n for n, on in
                                                 (("W2", not args.no_transpose_w2 and not mx),
-                                                 ("W1p", args.transpose_w1 and not mx)) if on],
+                                                 ("W1p", not args.no_transpose_w1 and not mx))
+                                                if on],
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "gemm_only_tflops": round(total_flops / gemm_ms / 1e9, 2),

@@ -16,10 +16,10 @@ permuted copy Xp is never written; FC1 and FC1's weight gradient read each row
 of x through src_row, so the forward keeps a reference to x for the backward
 (x must not change in between).  ``fuse_permute=False`` materializes Xp.
 
-Transposed weights for the dgrads (``transpose_w2``, default on;
-``transpose_w1``): at the start of each backward W2 (and W1p) are copied
-transposed (``moe_transpose_weights``), so FC2's dgrad + dGLU (and FC1's
-dgrad) read both operands contiguous along the reduction; the results are
+Transposed weights for the dgrads (``transpose_w2``, ``transpose_w1``, both
+on by default): at the start of each backward W2 and W1p are copied
+transposed (``moe_transpose_weights``), so FC2's dgrad + dGLU and FC1's dgrad
+read both operands contiguous along the reduction; the results are
 bit-identical to reading the weights as stored.
 
 Activation recomputation (``recompute=True``): the forward does not write
@@ -66,7 +66,7 @@ class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
-                 recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=False):
+                 recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=True):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
             raise ValueError(gemm)
