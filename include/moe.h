@@ -28,7 +28,10 @@
  *         scheduling and a configurable limit on the compute units a kernel uses.
  *  [P2] "JAXとNVIDIA Transformer EngineによるDropless MoE学習の高速化",
  *       section "主張と根拠": dropless MoE over ragged tensors, one grouped GEMM
- *       call over all ragged groups.
+ *       call over all ragged groups; tokens are dispatched to the experts and
+ *       their results combined.
+ *  [P3] "FlashMoE: Fast Distributed MoE in a Single Kernel", Abstract: a MoE
+ *       operator as dispatch, expert compute and combine phases.
  *
  * Conventions (all entry points):
  *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -123,10 +126,20 @@ int moe_glu_granularity(void);
 moe_status_t moe_route_topk(const float* logits, int T, int E, int k, int score, int normalize,
                             int32_t* topk_idx, float* topk_w, int32_t* err_word, void* stream);
 
-/* a7.  Gradient of the gate weights with respect to the logits.
+/* a7.  Gradient of the gate weights with respect to the logits.  The pages
+ * name the router only as part of the MoE block [P1 "MoE ブロックにおける
+ * トレーニングのボトルネック克服"] and give no gate formula; the gate
+ * functions are the reading stated at moe_route_topk (softmax over the
+ * selection, or sigmoid normalised over it), and this is their exact
+ * Jacobian-vector product: the selection itself is piecewise constant.
+ *   softmax, normalised:  dl_j = w_j (dw_j - sum_i w_i dw_i) for selected j;
+ *   sigmoid, normalised:  dl_j = s_j (1 - s_j) / S (dw_j - sum_i w_i dw_i),
+ *                         s = sigmoid(l), S = sum over the selection.
+ *   logits   [T, E] float32 (in, the forward's logits); topk_idx [T, k] (in)
  *   d_topk_w [T, k] float32 (in): dLoss/dtopk_w;  d_logits [T, E] float32
  *   (out, fully overwritten; 0 for unselected experts except for the
- *   unnormalised softmax, whose denominator involves every logit). */
+ *   unnormalised softmax, whose denominator involves every logit).
+ * Argument errors (null pointers, k out of range) return a status code. */
 moe_status_t moe_route_topk_bwd(const float* logits, const int32_t* topk_idx,
                                 const float* d_topk_w, int T, int E, int k, int score,
                                 int normalize, float* d_logits, void* stream);
@@ -235,8 +248,14 @@ typedef struct {
 moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* args, void* stream);
 
 /* a4.  Plain grouped GEMM ("linear"): y[r] = a[r] @ w[e]^T + b[e]
+ * [P2 "主張と根拠": the ragged groups of all experts in one grouped-GEMM
+ * call; P1 "MoE ブロックにおけるトレーニングのボトルネック克服": FC2 of the
+ * expert MLP, and the GroupGemm + Quantize family for the MX output option
+ * below].  Row r belongs to the expert e whose segment holds it.
  *   a [R, K] dtype;  w [E, N, K] dtype;  b [E, N] float32 nullable;
- *   y [R, N] dtype.  (FC2: K = f, N = d.) */
+ *   y [R, N] dtype.  (FC2: K = f, N = d.)
+ * Argument errors (null or misaligned pointers, N or K not a multiple of 8)
+ * return MOE_ERR_INVALID_ARG before anything is enqueued. */
 typedef struct {
   size_t struct_size; /* = sizeof(moe_gemm_fwd_args_t) */
   int dtype;
@@ -297,13 +316,18 @@ typedef struct {
 } moe_glu_bwd_args_t;
 moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* args, void* stream);
 
-/* a9 / a10 / a11.  Backward of the grouped linear map y = a @ w[e]^T (+ b[e]):
+/* a9 / a10 / a11.  Backward of the grouped linear map y = a @ w[e]^T (+ b[e])
+ * [P1 "融合された GEMM エピローグによる GLU 活性化関数の最適化": the backward
+ * pass of the expert MLP's grouped GEMMs (FC2's weight gradient, FC1's input
+ * and weight gradients); P2 "主張と根拠": one call over all ragged expert
+ * groups, the weight gradient reducing over each expert's rows]:
  *   DGRAD: da[r] = g[r] @ w[e]                 g [R, N], w [E, N, K] dtype,
  *          da [R, K] dtype (out).
  *   WGRAD: dw[e] = g[seg e]^T @ a[seg e]       g [R, N], a [R, K] dtype,
  *          dw [E, N, K] float32 (out; exact zeros for empty experts; added to
  *          the existing values when `accumulate`), db [E, N] float32
- *          (out, nullable): column sums of g over each segment. */
+ *          (out, nullable): column sums of g over each segment (added to
+ *          the existing values when `accumulate`, like dw). */
 typedef struct {
   size_t struct_size; /* = sizeof(moe_gemm_bwd_args_t) */
   int dtype;
@@ -433,9 +457,16 @@ moe_status_t moe_mxfp4_quantize_experts(const void* x, int dtype, const int32_t*
                                         void* stream);
 
 /* ---------------------------------------------------------------- combine
- * a5 / a12.  out[t] = sum_{j=0..k-1} topk_w[t,j] * y[row_map[t,j]], summed in
- * float32 in slot order (topk_w NULL: unit weights, the unpermute-sum of the
- * backward).  y [T*k, d] dtype; out [T, d] dtype. */
+ * a5 / a12.  The weighted combine that closes the MoE layer ([P3] "FlashMoE:
+ * Fast Distributed MoE in a Single Kernel", Abstract, names the dispatch,
+ * compute and combine phases of a MoE operator; P2 "主張と根拠" the combine
+ * that collects the experts' results).  The pages do not define it; the
+ * reading taken here is the usual gate-weighted sum, deterministic:
+ *   out[t] = sum_{j=0..k-1} topk_w[t,j] * y[row_map[t,j]], summed in float32
+ * in slot order and rounded once, no atomics (topk_w NULL: unit weights, the
+ * unpermute-sum of the backward).  y [T*k, d] dtype; out [T, d] dtype;
+ * row_map [T, k] from moe_permute.  Argument errors (null or misaligned
+ * pointers, d * element size not a multiple of 16) return a status code. */
 moe_status_t moe_unpermute_combine(const void* y, int dtype, const int32_t* row_map,
                                    const float* topk_w, int T, int k, int d, void* out,
                                    void* stream);
@@ -448,9 +479,11 @@ moe_status_t moe_unpermute_combine_mx(const moe_mx_t* y, int y_dtype, const int3
                                       const float* topk_w, int T, int k, int d, void* out,
                                       int out_dtype, void* stream);
 
-/* a6.  Backward of the combine:
+/* a6.  Backward of the combine (the exact gradient of the reading stated at
+ * moe_unpermute_combine; pages as there):
  *   d_y[row_map[t,j]]  = topk_w[t,j] * d_out[t]        (dtype, rounded once)
- *   d_topk_w[t,j]      = <d_out[t], y[row_map[t,j]]>   (float32)
+ *   d_topk_w[t,j]      = <d_out[t], y[row_map[t,j]]>   (float32, summed in a
+ *                        fixed order)
  * d_out [T, d], y [T*k, d], d_y [T*k, d] dtype.  d_y or d_topk_w may be NULL
  * (an MXFP8 layer writes dY only as MXFP8 copies, with moe_mx_quantize_experts). */
 moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dtype,

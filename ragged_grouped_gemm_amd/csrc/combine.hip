@@ -178,41 +178,100 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel_k(
 }
 
 // Bias gradient of a grouped linear map: db[e][n] = sum over the rows of
-// segment e of g[r][n], float32, rows summed in order (deterministic).
-// grid: (ceil(N / 256), E); each thread owns one column.
+// segment e of g[r][n], float32 (added to db when `accumulate`).
+// grid: (ceil(N / CS_COLS), E), 1024 threads.  A block owns CS_COLS columns
+// of one expert; a lane owns one 16-byte chunk (V columns) of every CS_RPW-th
+// row of the wave's share, the 16 waves take interleaved groups of CS_RPW rows,
+// so the segment is read in whole 128-byte pieces by the whole block at once
+// (the sum is HBM-bound, not latency-bound, even for a 16K-row expert).  The
+// partial sums are combined in a fixed order -- a butterfly over the row
+// slots of a wave, then the waves in order -- so the result does not depend
+// on timing.
+static constexpr int CS_LPR = 8;                  // lanes per row (8 x 16 bytes)
+static constexpr int CS_RPW = 64 / CS_LPR;        // rows per wave instruction
+static constexpr int CS_WAVES = 16;
+
 template <class EL>
-__global__ void __launch_bounds__(256) segment_colsum_kernel(const typename EL::storage* g,
-                                                             const int32_t* __restrict__ offsets,
-                                                             int R, int N, float* db) {
-  int n = blockIdx.x * 256 + threadIdx.x;
-  int e = blockIdx.y;
-  if (n >= N) return;
-  int s = min(max(offsets[e], 0), R), t = min(max(offsets[e + 1], 0), R);
-  float acc = 0.0f;
-  for (int r = s; r < t; ++r) {
-    float v;
-    if constexpr (EL::VEC == 8)
-      v = bf16_bits_to_f32(g[(size_t)r * N + n]);
-    else
-      v = g[(size_t)r * N + n];
-    acc += v;
+__global__ void __launch_bounds__(1024) segment_colsum_kernel(const typename EL::storage* g,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int R, int N, float* db,
+                                                              int accumulate) {
+  constexpr int V = EL::VEC;
+  constexpr int COLS = CS_LPR * V;
+  __shared__ float part[CS_WAVES][COLS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane % CS_LPR, slot = lane / CS_LPR;
+  const int e = blockIdx.y;
+  const int col = blockIdx.x * COLS + c * V;
+  const int s = min(max(offsets[e], 0), R), t = min(max(offsets[e + 1], s), R);
+  float acc[V], acc2[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q) acc[q] = acc2[q] = 0.0f;
+  if (col < N) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(g + col);
+    const size_t ld = (size_t)N * sizeof(typename EL::storage) / 16;   // row stride in chunks
+    constexpr int STEP = CS_WAVES * CS_RPW;
+    int r = s + w * CS_RPW + slot;
+    // two rows in flight per lane, summed into two accumulators in a fixed order
+    for (; r + STEP < t; r += 2 * STEP) {
+      const u32x4 a = src[(size_t)r * ld], b = src[(size_t)(r + STEP) * ld];
+      float va[V], vb[V];
+      unpack_chunk(a, va, EL());
+      unpack_chunk(b, vb, EL());
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        acc[q] += va[q];
+        acc2[q] += vb[q];
+      }
+    }
+    if (r < t) {
+      float va[V];
+      unpack_chunk(src[(size_t)r * ld], va, EL());
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] += va[q];
+    }
   }
-  db[(size_t)e * N + n] = acc;
+#pragma unroll
+  for (int q = 0; q < V; ++q) {
+    float v = acc[q] + acc2[q];
+    // the row slots of the wave: lanes that differ in bits 3..5
+#pragma unroll
+    for (int o = CS_LPR; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    acc[q] = v;
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int q = 0; q < V; ++q) part[w][c * V + q] = acc[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < COLS) {
+    const int n = blockIdx.x * COLS + threadIdx.x;
+    if (n < N) {
+      float tot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CS_WAVES; ++i) tot += part[i][threadIdx.x];
+      float* o = db + (size_t)e * N + n;
+      *o = accumulate ? *o + tot : tot;
+    }
+  }
 }
 
 template __global__ void segment_colsum_kernel<BF16>(const uint16_t*, const int32_t*, int, int,
-                                                     float*);
-template __global__ void segment_colsum_kernel<F32>(const float*, const int32_t*, int, int, float*);
+                                                     float*, int);
+template __global__ void segment_colsum_kernel<F32>(const float*, const int32_t*, int, int, float*,
+                                                    int);
 
 moe_status_t launch_segment_colsum(int dtype, const void* g, const int32_t* offsets, int E,
-                                   int R, int N, float* db, hipStream_t s) {
-  dim3 grid((N + 255) / 256, E);
+                                   int R, int N, float* db, int accumulate, hipStream_t s) {
+  // N is a multiple of 8, so rows are whole 16-byte chunks (bf16 and float32)
+  const int cols = CS_LPR * (dtype == MOE_BF16 ? BF16::VEC : F32::VEC);
+  dim3 grid((N + cols - 1) / cols, E);
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(segment_colsum_kernel<BF16>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t*>(g), offsets, R, N, db);
+    hipLaunchKernelGGL(segment_colsum_kernel<BF16>, grid, dim3(64 * CS_WAVES), 0, s,
+                       reinterpret_cast<const uint16_t*>(g), offsets, R, N, db, accumulate);
   else
-    hipLaunchKernelGGL(segment_colsum_kernel<F32>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const float*>(g), offsets, R, N, db);
+    hipLaunchKernelGGL(segment_colsum_kernel<F32>, grid, dim3(64 * CS_WAVES), 0, s,
+                       reinterpret_cast<const float*>(g), offsets, R, N, db, accumulate);
   return launch_status();
 }
 

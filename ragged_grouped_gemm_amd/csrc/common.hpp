@@ -121,9 +121,10 @@ inline bool valid_dtype(int dtype) { return dtype == MOE_F32 || dtype == MOE_BF1
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
-// db[e][n] = column sums of g [R, N] over the rows of expert segment e (float32).
+// db[e][n] = column sums of g [R, N] over the rows of expert segment e
+// (float32; added to db when accumulate).
 moe_status_t launch_segment_colsum(int dtype, const void* g, const int32_t* offsets, int E,
-                                   int R, int N, float* db, hipStream_t s);
+                                   int R, int N, float* db, int accumulate, hipStream_t s);
 
 }  // namespace moe
 

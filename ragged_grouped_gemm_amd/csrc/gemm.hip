@@ -1634,8 +1634,9 @@ moe_status_t launch_gemm(const GemmArgs& p, int max_cus, hipStream_t s) {
 //    extra registers do not fit under the 16-wave limit of 128 VGPRs).
 // Each choice is the fastest of a same-process sweep at the DeepSeek-V3-like
 // shard.  Small or narrow problems take 128 x 128, fp32 takes 64 x 128.
-// MOE_GEMM_TILE=<n> in the environment selects variant n of the list below
-// for bf16 instead (tuning sweeps).
+// A library built with -DMOE_GEMM_TUNING (for tuning sweeps only) reads
+// MOE_GEMM_TILE=<n> from the environment and takes variant n of the list
+// below for bf16 instead; the product library never reads the environment.
 typedef Tile<256, 256, 4, 4, 128, 2, 1> TBig;
 typedef Tile<256, 256, 2, 4, 128, 2, 1> TBigGlu;
 typedef Tile<256, 256, 2, 4, 128, 2, 2> TBigPingPong;
@@ -1643,8 +1644,12 @@ typedef Tile<128, 128, 2, 2, 128, 2> TSmall;
 typedef Tile<64, 128, 2, 2, 128, 2> TF32;
 
 inline int tile_variant() {
+#ifdef MOE_GEMM_TUNING
   const char* v = getenv("MOE_GEMM_TILE");
   return v ? atoi(v) : -1;
+#else
+  return -1;
+#endif
 }
 
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI, bool GATHER = false>
@@ -1711,19 +1716,22 @@ moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipSt
   return dispatch_tiles<F32, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
 }
 
-// MOE_GEMM_GM in the environment overrides the band height, MOE_GEMM_SNAKE=0
-// turns the weight gradients' alternating tile order off (for tuning).
+// Band height 4 and the weight gradients' alternating tile order.  (A
+// -DMOE_GEMM_TUNING build lets MOE_GEMM_GM override the band height and
+// MOE_GEMM_SNAKE=0 turn the alternating order off, for tuning sweeps.)
 inline GemmArgs zero_args() {
   GemmArgs p;
   memset(&p, 0, sizeof(p));
   p.alpha = 1.0f;
   p.gm = 4;
+  p.snake = 1;
+#ifdef MOE_GEMM_TUNING
   if (const char* v = getenv("MOE_GEMM_GM")) {
     int g = atoi(v);
     if (g >= 1 && g <= 64) p.gm = g;
   }
-  p.snake = 1;
   if (const char* v = getenv("MOE_GEMM_SNAKE")) p.snake = atoi(v) != 0;
+#endif
   return p;
 }
 
@@ -2144,7 +2152,8 @@ moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {
   moe_status_t st = dispatch<false, false, RAGGED_K, EPI_STORE>(
       a->dtype, p, big_ragged_k(a->R, a->E, a->N, a->K), a->max_cus, s);
   if (st != MOE_OK || !a->db) return st;
-  return launch_segment_colsum(a->dtype, a->g, a->offsets, a->E, a->R, a->N, a->db, s);
+  return launch_segment_colsum(a->dtype, a->g, a->offsets, a->E, a->R, a->N, a->db,
+                               a->accumulate, s);
 }
 
 }  // extern "C"

@@ -14,7 +14,10 @@ unpermute-sum (dX).
 Gather-fused permute (``fuse_permute``, the default for bf16 / float32): the
 permuted copy Xp is never written; FC1 and FC1's weight gradient read each row
 of x through src_row, so the forward keeps a reference to x for the backward
-(x must not change in between).  ``fuse_permute=False`` materializes Xp.
+(x must not change in between).  ``fuse_permute=False`` materializes Xp.  The
+gathering loaders address x with 31-bit byte offsets from one base, so a
+layer whose x spans 2 GiB or more (e.g. 150K tokens at d = 7168 in bf16)
+materializes Xp whatever ``fuse_permute`` says (``gather_fits``).
 
 Transposed weights for the dgrads (``transpose_w2``, ``transpose_w1``, both
 on by default): at the start of each backward W2 and W1p are copied
@@ -63,6 +66,14 @@ class MXWeights:
 
 
 class MoEFFN:
+    # largest x (bytes) the gather-fused loaders can address from one base
+    GATHER_MAX_BYTES = 0x7FFFFFF0
+
+    @staticmethod
+    def gather_fits(T, d, dtype) -> bool:
+        """Whether x [T, d] is small enough for the gather-fused permute."""
+        return T * d * torch.empty((), dtype=dtype).element_size() <= MoEFFN.GATHER_MAX_BYTES
+
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
@@ -79,7 +90,7 @@ class MoEFFN:
             raise ValueError("recompute applies to the bf16 / fp32 training layer")
         self.recompute = recompute
         self.W1p_saved = self.b1p_saved = None
-        self.fuse_permute = fuse_permute and not self.mx
+        self.fuse_permute = fuse_permute and not self.mx and self.gather_fits(T, d, dtype)
         self.x_saved = None
         if self.mx and (bias or act == "srelu" or dtype != torch.bfloat16):
             raise ValueError("the MXFP8 variant is gated, bias-free, with bf16 activations")

@@ -208,3 +208,21 @@ def test_struct_layouts_match_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def test_layer_materializes_xp_when_x_is_too_large_to_gather():
+    """The gather-fused loaders address x with 31-bit offsets: a layer whose x
+    spans 2 GiB or more takes the materialized-Xp path (built on the meta
+    device, so nothing is allocated or run)."""
+    import torch
+    from ragged_grouped_gemm_amd.layer import MoEFFN
+    small = MoEFFN(16384, 7168, 2048, 32, 8, device="meta")
+    assert small.fuse_permute and small.xp is None
+    T = 160_000                      # 160000 * 7168 * 2 bytes > 2 GiB
+    assert not MoEFFN.gather_fits(T, 7168, torch.bfloat16)
+    big = MoEFFN(T, 7168, 2048, 32, 1, device="meta")
+    assert not big.fuse_permute
+    assert big.xp is not None and tuple(big.xp.shape) == (T, 7168)
+    # a float32 x reaches the limit at half the tokens
+    assert MoEFFN.gather_fits(80_000, 7168, torch.bfloat16)
+    assert not MoEFFN.gather_fits(80_000, 7168, torch.float32)

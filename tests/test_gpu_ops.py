@@ -299,7 +299,8 @@ def test_gemm_dgrad(dtype, counts, N, K):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("counts,N,K", [(COUNTS_SMALL, 512, 256), (COUNTS_BIG, 1024, 1024),
-                                        (COUNTS_SMALL, 2880, 96)])
+                                        (COUNTS_SMALL, 2880, 96),
+                                        ([0, 16352, 5, 129, 0, 1], 200, 64)])
 def test_gemm_wgrad(dtype, counts, N, K):
     note(f"gemm wgrad {dtype} R={sum(counts)} N={N} K={K}")
     rng, off, offd = _setup(counts, N + 7 * K)
@@ -308,9 +309,9 @@ def test_gemm_wgrad(dtype, counts, N, K):
     gh, gd = mk(rng, (R, N))
     ah, ad = mk(rng, (R, K))
     dw, db = ops.moe_grouped_gemm_bwd(gd, offd, mode="wgrad", a=ad, want_db=True)
-    # accumulate: a second call adds to the first result
-    dw2 = dw.clone()
-    ops.moe_grouped_gemm_bwd(gd, offd, mode="wgrad", a=ad, out=dw2, accumulate=True)
+    # accumulate: a second call adds to the first result, bias gradient included
+    dw2, db2 = dw.clone(), db.clone()
+    ops.moe_grouped_gemm_bwd(gd, offd, mode="wgrad", a=ad, out=dw2, db=db2, accumulate=True)
     torch.cuda.synchronize()
     ref, refb = om.grouped_wgrad(gh, ah, off, with_bias=True)
     got = host(dw)
@@ -320,6 +321,7 @@ def test_gemm_wgrad(dtype, counts, N, K):
         if c == 0:
             assert not got[e].any() and not host(db)[e].any()     # exact zeros
     assert f32_ok(host(dw2), 2 * ref)
+    assert f32_ok(host(db2), 2 * refb)
 
 
 # ------------------------------------------------------------------ combine
