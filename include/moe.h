@@ -166,6 +166,28 @@ moe_status_t moe_permute(const void* x, int dtype, int T, int d, const int32_t* 
                          int32_t* pad_offsets, int32_t* row_map, int32_t* src_row, void* xp,
                          void* ws, size_t ws_bytes, int32_t* err_word, void* stream);
 
+/* a2 without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Computes exactly what moe_permute computes, with the same
+ * arguments except ws / ws_bytes: the per-chunk counts live in a static
+ * device array of MOE_PERMUTE_NOALLOC_MAX_BYTES bytes inside the library,
+ * one per GPU, held until the process ends.  The call allocates and frees
+ * nothing; its first call on a device looks up that device's copy of the
+ * array (make one call before capturing a graph).
+ *   Limit: moe_permute_workspace_size(T, E, k) <= MOE_PERMUTE_NOALLOC_MAX_BYTES,
+ *   i.e. ceil(T*k / 1024) * E <= 262144 (for example T*k <= 8M at E = 32,
+ *   T*k <= 256K at E = 1024); larger sizes return MOE_ERR_WORKSPACE before
+ *   anything is enqueued.
+ *   Every call on one GPU uses the same array (nothing in it needs clearing:
+ *   each call writes every entry before reading it), so calls that overlap on
+ *   one GPU -- on different streams, or from different host threads without
+ *   ordering -- race and must not be made. */
+#define MOE_PERMUTE_NOALLOC_MAX_BYTES (1 << 20)
+moe_status_t moe_permute_noalloc(const void* x, int dtype, int T, int d,
+                                 const int32_t* topk_idx, int k, int E, int32_t* counts,
+                                 int32_t* offsets, int32_t* pad_offsets, int32_t* row_map,
+                                 int32_t* src_row, void* xp, int32_t* err_word, void* stream);
+
 /* ---------------------------------------------------------------- repack
  * a13.  FC1 weight repack [P1 "融合された GEMM エピローグ…", Figure 2].
  * Canonical W1 rows [0, f) are the gate chunk (activated) and [f, 2f) the

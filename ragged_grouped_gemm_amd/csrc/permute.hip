@@ -20,6 +20,8 @@
 //   4. gather:  xp[r] = x[src_row[r]], one wave per row, 16-byte vectors.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace moe {
 
 static constexpr int PERM_THREADS = 256;
@@ -162,38 +164,15 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(const u32x4* __restric
   for (int c = lane; c < chunks_per_row; c += 64) dst[c] = src[c];
 }
 
-}  // namespace moe
-
-using namespace moe;
-
-extern "C" {
-
-size_t moe_permute_workspace_size(int T, int E, int k) {
-  if (T <= 0 || E <= 0 || k <= 0) return 256;
-  size_t n = (size_t)T * k;
-  size_t nchunks = (n + CHUNK - 1) / CHUNK;
-  return (nchunks * (size_t)E * sizeof(int32_t) + 255) / 256 * 256;
-}
-
-moe_status_t moe_permute(const void* x, int dtype, int T, int d, const int32_t* topk_idx,
-                         int k, int E, int32_t* counts, int32_t* offsets,
-                         int32_t* pad_offsets, int32_t* row_map, int32_t* src_row, void* xp,
-                         void* ws, size_t ws_bytes, int32_t* err_word, void* stream) {
-  MOE_CHECK_ARG(T >= 0 && E >= 1 && E <= MOE_MAX_EXPERTS && k >= 1 && k <= E);
-  MOE_CHECK_ARG(counts && offsets);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  size_t n = (size_t)T * k;
-  MOE_CHECK_ARG(n < (size_t)INT32_MAX);
-  if (xp) {
-    MOE_CHECK_ARG(x && valid_dtype(dtype) && d > 0);
-    MOE_CHECK_ARG(aligned16(x) && aligned16(xp) && (d * dtype_size(dtype)) % 16 == 0);
-  }
-  if (n > 0) {
-    MOE_CHECK_ARG(topk_idx && row_map && src_row && ws);
-    if (ws_bytes < moe_permute_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
-  }
-  int nchunks = (int)((n + CHUNK - 1) / CHUNK);
-  int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws);
+// The four kernels above on the caller's stream; ws holds the per-chunk,
+// per-expert counts (every entry is written by the count kernel before it
+// is read, so ws needs no clearing).
+static moe_status_t permute_run(const void* x, int dtype, int T, int d, const int32_t* topk_idx, int k,
+                         int E, int32_t* counts, int32_t* offsets, int32_t* pad_offsets,
+                         int32_t* row_map, int32_t* src_row, void* xp, int32_t* chunk_counts,
+                         int32_t* err_word, hipStream_t s) {
+  const size_t n = (size_t)T * k;
+  const int nchunks = (int)((n + CHUNK - 1) / CHUNK);
   if (nchunks > 0) {
     hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(PERM_THREADS),
                        E * sizeof(int32_t), s, topk_idx, (int)n, E, chunk_counts, err_word);
@@ -216,6 +195,94 @@ moe_status_t moe_permute(const void* x, int dtype, int T, int d, const int32_t* 
     }
   }
   return MOE_OK;
+}
+
+// Argument checks shared by both entry points.
+static moe_status_t permute_check(const void* x, int dtype, int T, int d, const int32_t* topk_idx,
+                           int k, int E, int32_t* counts, int32_t* offsets, int32_t* row_map,
+                           int32_t* src_row, void* xp) {
+  MOE_CHECK_ARG(T >= 0 && E >= 1 && E <= MOE_MAX_EXPERTS && k >= 1 && k <= E);
+  MOE_CHECK_ARG(counts && offsets);
+  MOE_CHECK_ARG((size_t)T * k < (size_t)INT32_MAX);
+  if (xp) {
+    MOE_CHECK_ARG(x && valid_dtype(dtype) && d > 0);
+    MOE_CHECK_ARG(aligned16(x) && aligned16(xp) && (d * dtype_size(dtype)) % 16 == 0);
+  }
+  if (T > 0) MOE_CHECK_ARG(topk_idx && row_map && src_row);
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+// Scratch of the allocation-free permute (moe_permute_noalloc): the
+// per-chunk, per-expert counts that moe_permute keeps in the caller's
+// workspace.  Each device holds its own copy until the process ends; in host
+// code `scratch` names only a host-side stand-in, so the device address is
+// looked up once per device (hipGetSymbolAddress) and only that is used.
+static constexpr size_t kPermuteScratchBytes = MOE_PERMUTE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) int32_t scratch[kPermuteScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The current device's address of `scratch` (looked up on its first use).
+moe_status_t scratch_on_current_device(int32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_permute_workspace_size(int T, int E, int k) {
+  if (T <= 0 || E <= 0 || k <= 0) return 256;
+  size_t n = (size_t)T * k;
+  size_t nchunks = (n + CHUNK - 1) / CHUNK;
+  return (nchunks * (size_t)E * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+moe_status_t moe_permute(const void* x, int dtype, int T, int d, const int32_t* topk_idx,
+                         int k, int E, int32_t* counts, int32_t* offsets,
+                         int32_t* pad_offsets, int32_t* row_map, int32_t* src_row, void* xp,
+                         void* ws, size_t ws_bytes, int32_t* err_word, void* stream) {
+  moe_status_t st =
+      permute_check(x, dtype, T, d, topk_idx, k, E, counts, offsets, row_map, src_row, xp);
+  if (st != MOE_OK) return st;
+  if (T > 0) {
+    MOE_CHECK_ARG(ws);
+    if (ws_bytes < moe_permute_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
+  }
+  return permute_run(x, dtype, T, d, topk_idx, k, E, counts, offsets, pad_offsets, row_map,
+                     src_row, xp, reinterpret_cast<int32_t*>(ws), err_word,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_permute_noalloc(const void* x, int dtype, int T, int d,
+                                 const int32_t* topk_idx, int k, int E, int32_t* counts,
+                                 int32_t* offsets, int32_t* pad_offsets, int32_t* row_map,
+                                 int32_t* src_row, void* xp, int32_t* err_word, void* stream) {
+  moe_status_t st =
+      permute_check(x, dtype, T, d, topk_idx, k, E, counts, offsets, row_map, src_row, xp);
+  if (st != MOE_OK) return st;
+  // sizes beyond the static scratch are refused before anything touches the device
+  if (moe_permute_workspace_size(T, E, k) > kPermuteScratchBytes) return MOE_ERR_WORKSPACE;
+  int32_t* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != MOE_OK) return st;
+  return permute_run(x, dtype, T, d, topk_idx, k, E, counts, offsets, pad_offsets, row_map,
+                     src_row, xp, ws, err_word, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

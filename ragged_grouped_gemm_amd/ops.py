@@ -196,6 +196,23 @@ def moe_permute(x, topk_idx, E, *, counts=None, offsets=None, pad_offsets=None, 
     return counts, offsets, pad_offsets, row_map, src_row, xp
 
 
+def moe_permute_noalloc(x, topk_idx, E, *, counts, offsets, row_map, src_row, pad_offsets=None,
+                        xp=None, err_word=None):
+    """moe_permute with the library's static scratch instead of a workspace:
+    every output is the caller's preallocated tensor and the call allocates
+    nothing (the first call on a device looks up the scratch address).  With
+    xp given, x is gathered into it."""
+    T, k = topk_idx.shape
+    d = x.shape[1] if xp is not None else 0
+    dt = _dtype(x) if xp is not None else _lib.MOE_BF16
+    check(_lib.load().moe_permute_noalloc(_p(x) if xp is not None else None, dt, T, d,
+                                          _p(topk_idx), k, E, _p(counts), _p(offsets),
+                                          _p(pad_offsets), _p(row_map), _p(src_row), _p(xp),
+                                          _p(err_word), _stream()),
+          "moe_permute_noalloc")
+    return counts, offsets, pad_offsets, row_map, src_row, xp
+
+
 def moe_repack_glu_weights(w, b=None, inverse=False, w_out=None, b_out=None):
     E, n1, d = w.shape
     f = n1 // 2
