@@ -1002,6 +1002,14 @@ struct GemmCfg {
   static constexpr int MX_STAGE_FLOATS = 32 * 36;
   static constexpr int STAGE_WAVES = STAGE_U4 * 16 / (MX_STAGE_FLOATS * 4);
   static constexpr int MX_SLOTS = (THREADS / 64 + STAGE_WAVES - 1) / STAGE_WAVES;
+  // The plain epilogue can stage 32 rows of each wave's tile (in the output
+  // type OT) in the free ring slot before writing whole rows, where every
+  // wave's rows fit in it.
+  template <class OT>
+  static constexpr bool stage_fits() {
+    return (THREADS / 64) * 32 * WTN * (int)sizeof(OT) <= STAGE_U4 * 16 &&
+           (WTN * (int)sizeof(OT) == 128 || WTN * (int)sizeof(OT) == 256);
+  }
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!epi_glu_fwd(EPI) || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
   static_assert(LDS_BYTES + 8320 <= 160 * 1024, "LDS ring does not fit");
@@ -1415,6 +1423,16 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     // ---- epilogue: lane holds rows (lane & 31) + 32 i, columns 32 j + 8 g + 4 h + q ----
     typedef typename OutT<EL>::type SO;
     const int cw = n0 + wn * C::WTN + 4 * (lane >> 5);  // column of the lane's first value
+    // output element of the plain epilogue: the storage type (RAGGED_M) or
+    // float32 (weight gradients)
+    typedef typename std::conditional<GROUP == RAGGED_M, SO, float>::type OT;
+    // (built where it needs no spills: the plain bf16 epilogue of tiles with
+    // both operands K-contiguous and the pinned or compiler schedule -- FC2
+    // and the FC1 dgrad from the transposed weights -- whose direct stores
+    // wrote 1.58x the output bytes; the weight gradients' float32 stores
+    // already reach 1.03-1.08x)
+    constexpr bool kStaged = EPI == EPI_STORE && GROUP == RAGGED_M && !MX && AKM && BKM &&
+                             TL::SCHED != 2 && C::template stage_fits<OT>();
     bool mx_store = false;  // plain product written as an MX row copy instead of C
     if constexpr (MX && EPI == EPI_STORE && GROUP == RAGGED_M) mx_store = p.mxr != nullptr;
     if (mx_store) {
@@ -1552,6 +1570,64 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                                           p.clamp, p.alpha, p.gelu_tanh);
         }
       });
+    } else if (kStaged && !(GROUP == RAGGED_K && p.accumulate)) {
+      if constexpr (kStaged) {
+        // Plain epilogue through LDS: each wave stages 32 rows x WTN columns of
+        // its tile at a time in the ring slot that no wave reads any more
+        // (nk % STAGES: its last reader passed the barrier of the last step,
+        // and no load is in flight into it; the next tile's loads start after
+        // the tile barrier), then writes whole rows -- 16 bytes per lane, a
+        // row's WTN columns contiguous -- instead of 16-byte pieces of 32 rows
+        // per store.  Chunk c (16 bytes) of staged row r sits at c ^ ((r >> 1)
+        // & 7) for 128-byte rows or c ^ (r & 15) for 256-byte rows, so the
+        // accumulator writes (32 rows, one chunk each) and the row reads touch
+        // each bank at most twice.  Same values and rounding as the direct path.
+        constexpr int OB = (int)sizeof(OT);
+        constexpr int CPRW = C::WTN * OB / 16;     // 16-byte chunks per staged row
+        constexpr int EPC = 16 / OB;               // elements per chunk
+        constexpr int RPI = 64 / CPRW;             // staged rows per wave instruction
+        auto slot = [](int r, int c) { return CPRW == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
+        u32x4* Wt = stage_ptr(nk) + wave * 32 * CPRW;
+        char* Wb = reinterpret_cast<char*>(Wt);
+        const float* bias = (GROUP == RAGGED_M && p.bias) ? p.bias + (size_t)e * p.ld_bias : nullptr;
+        OT* Cg = reinterpret_cast<OT*>(p.c);
+        if constexpr (GROUP == RAGGED_K) Cg += (size_t)e * p.c_expert_stride;
+        const int r = lane & 31, h = lane >> 5;
+        static_for<0, TM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          static_for<0, TN>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int cl = 32 * j + 8 * g + 4 * h;   // column within the wave tile
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = acc[i][j][4 * g + q];
+                if (bias && cw + 32 * j + 8 * g + q < p.N) v[q] += bias[cw + 32 * j + 8 * g + q];
+              }
+              if constexpr (OB == 2) {
+                const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *reinterpret_cast<u32x2*>(Wb + (r * CPRW + slot(r, cl / 8)) * 16 + (cl % 8) * 2) = w;
+              } else {
+                Wt[r * CPRW + slot(r, cl / 4)] = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                       __float_as_uint(v[2]), __float_as_uint(v[3])};
+              }
+            }
+          });
+          wave_lds_sync();
+#pragma unroll
+          for (int it = 0; it < 32 / RPI; ++it) {
+            const int rr = it * RPI + lane / CPRW, cc = lane % CPRW;
+            const u32x4 v = Wt[rr * CPRW + slot(rr, cc)];
+            const int row = m0 + wm * C::WTM + 32 * i + rr;
+            const int col = n0 + wn * C::WTN + cc * EPC;
+            if (row < mlim && col < p.N)
+              *reinterpret_cast<u32x4*>(Cg + (size_t)row * p.ldc + col) = v;
+          }
+          wave_lds_sync();
+        });
+      }
     } else
     static_for<0, TM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
