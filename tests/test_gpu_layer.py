@@ -8,7 +8,9 @@ final rounding, and the occasional one-ulp flip where the library's float32
 value and the oracle's float64 value round to neighbouring bf16 values.
 Tolerances:
   * routing and layout: bit-exact; gates: relative L2 <= 1e-5;
-  * float32 workloads: every tensor relative L2 <= 1e-5;
+  * float32 workloads: every tensor relative L2 <= 1e-5, and every layer
+    output and gradient also max |err| / rms <= 1e-5 (measured on the
+    MI355X: at most 5.3e-6, dW2 of tiny_fp32);
   * bf16 workloads, layer outputs stored in bf16 (out, dX): max |err| beyond
     the output's own half-ulp rounding, / rms, <= 2e-2 (raw max|err|/rms and
     the rounding floor are printed beside it);
@@ -137,6 +139,7 @@ def test_layer_parity(name, fused):
             report[label] = e
             report[label + "_max"] = norm_err(got, ref)
             assert e <= 1e-5, (label, e, report)
+            assert report[label + "_max"] <= 1e-5, (label, report)
             return
         raw = norm_err(got, ref)
         bf16_store = label in ("out", "dX")
