@@ -191,6 +191,22 @@ def route_topk_bwd(logits, idx, dw, score: str = "softmax", normalize: bool = Tr
     return dl
 
 
+def router_logits(x, Wr):
+    """The router's linear map: logits[t, e] = <x[t], Wr[e]> (no bias).
+
+    [P1 Bottlenecks]: routing decides at run time which experts each token
+    reaches; the logits it ranks come from this map of the layer's own input.
+    """
+    return _f64(x) @ _f64(Wr).T
+
+
+def router_backward(dlogits, x, Wr):
+    """Gradients of :func:`router_logits` given dL/dlogits:
+    dWr[e] = sum_t dlogits[t, e] x[t],  dx[t] = sum_e dlogits[t, e] Wr[e]."""
+    dl = _f64(dlogits)
+    return dl.T @ _f64(x), dl @ _f64(Wr)
+
+
 # ---------------------------------------------------------------------------
 # a2: permute into expert-contiguous rows  [P2 "主張と根拠": ragged groups;
 #     P1 Sync: counts in device memory]
@@ -567,10 +583,16 @@ def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
     return res
 
 
-def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias=False):
+def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias=False,
+                   router=None):
     """Backward chain matching :func:`layer_forward`: the exact gradient of the
     grouped formulation, with the stored tensors (dY, dH, dXp, dX) rounded to
-    ``spec.store`` and the weight / bias / gate gradients kept in float64."""
+    ``spec.store`` and the weight / bias / gate gradients kept in float64.
+
+    ``router=(x, Wr)`` when the logits are the router's map of x
+    (:func:`router_logits`): the router's gradients are added -- dWr, and
+    its share of dx, added to the experts' dX after that is stored:
+    dX = rnd(rnd(dX_experts) + dlogits Wr)."""
     rnd = storage_round(spec.store)
     offsets, row_map = fwd["offsets"], fwd["row_map"]
     q = spec.mx
@@ -614,6 +636,10 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
     dX = combine(dXp_s, row_map, None)
     out = dict(dY=dY_s, dgate=dgate, dlogits=dlogits, dA=dA, dH=dH_s, dW2=dW2, dXp=dXp_s,
                dW1=dW1, dX=rnd(dX), dY_exact=dY, dH_exact=dH, dXp_exact=dXp, dX_exact=dX)
+    if router is not None:
+        dWr, dx_r = router_backward(dlogits, router[0], router[1])
+        out.update(dWr=dWr, dX_router=dx_r, dX_experts=out["dX"],
+                   dX_exact=out["dX"] + dx_r, dX=rnd(out["dX"] + dx_r))
     if q:
         out.update(dY_col=dY_col, dH_col=dH_col)
     if has_bias:
