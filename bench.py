@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--no-transpose-w1", action="store_true",
                     help="bf16 / fp32 training workloads: FC1's dgrad reads W1p as stored "
                          "(MN-contiguous) instead of a transposed copy made in each backward")
+    ap.add_argument("--router", action="store_true",
+                    help="the layer computes its own logits: the router's map x w_router^T fused "
+                         "with the top-k routing (w_router synthetic N(0, 1/d), so the routing is "
+                         "not Zipf-skewed), and the router's backward (dWr, its share of dX)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -80,6 +84,7 @@ def hbm_bytes(cfg, fused_permute=False):
     b = 4 if cfg.dtype == "f32" else 2
     T, R, d, k, E = cfg.T, cfg.R, cfg.d, cfg.k, cfg.E
     out = {"route_topk": T * E * 4 + T * k * 8,
+           "router_topk": T * cfg.d * (4 if cfg.dtype == "f32" else 2) + T * E * 4 + T * k * 8,
            "permute": T * d * b + R * d * b + T * k * 4 + 8 * R,
            "combine": R * d * b + T * d * b + 8 * R}
     if fused_permute:
@@ -96,6 +101,7 @@ def hbm_bytes(cfg, fused_permute=False):
             out["quantize_dy"] = R * d * b + 2 * mxb(d) + 8 * R
         f, n1 = cfg.f, cfg.n1
         out.update({"transpose_w2": 2 * E * d * f * b, "transpose_w1p": 2 * E * d * n1 * b})
+        out["router_bwd"] = 3 * T * d * b + T * E * 4 + E * d * 4
         out.update({"combine_bwd": T * d * b + 2 * R * d * b + 12 * R,
                     "route_topk_bwd": T * E * 8 + T * k * 8,
                     "unpermute_dx": R * d * b + T * d * b + 4 * R})
@@ -203,7 +209,10 @@ def main():
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
                recompute=args.recompute, mx_dxp=args.mx_dxp,
-               transpose_w2=not args.no_transpose_w2, transpose_w1=not args.no_transpose_w1)
+               transpose_w2=not args.no_transpose_w2, transpose_w1=not args.no_transpose_w1,
+               router=args.router)
+    if args.router:
+        lg = t(synth.draw_router_weights(cfg))       # the layer's logits come from x lg^T
     permute = "fused" if L.fuse_permute else "copy"
     if mx:
         # the MXFP8 weight copies are made once, outside the timed steps (the
@@ -277,6 +286,7 @@ def main():
                    "k": cfg.k, "routed_rows": cfg.R, "score": cfg.score, "act": cfg.act,
                    "permute": "mx_quantize_gather" if mx else permute,
                    "recompute_fc1": bool(args.recompute),
+                   "fused_router": bool(args.router),
                    "mx_dxp": bool(args.mx_dxp),
                    "dgrad_weights_transposed": [n for n, on in
                                                 (("W2", not args.no_transpose_w2 and not mx),

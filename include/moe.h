@@ -144,6 +144,41 @@ moe_status_t moe_route_topk_bwd(const float* logits, const int32_t* topk_idx,
                                 const float* d_topk_w, int T, int E, int k, int score,
                                 int normalize, float* d_logits, void* stream);
 
+/* f4.  The router's linear map fused with top-k routing [P1 "MoE ブロックにおける
+ * トレーニングのボトルネック克服": the tokens per expert come out of routing at
+ * run time; P1 Figure 1: forward and backward fused into custom kernels].  The
+ * pages do not write the router out; the reading taken is a linear map of the
+ * layer's input without bias:
+ *   logits[t, e] = sum_c x[t, c] w_router[e, c]      (float32 accumulation)
+ * followed, in the same launch and from the logits held in LDS, by exactly
+ * the selection and gates of moe_route_topk (bit-identical to moe_route_topk
+ * on the same logits).
+ *   x [T, d], w_router [E, d]: dtype MOE_BF16 (MOE_F32: MOE_ERR_UNSUPPORTED),
+ *   d a multiple of 32, 16-byte aligned pointers.
+ *   logits   [T, E] float32 (out, nullable for E <= 256; the routing backward
+ *            needs it).  For E > 256 the logits are computed in passes of 256
+ *            experts and selected by moe_route_topk's kernel: logits required.
+ *   topk_idx [T, k], topk_w [T, k] (out, as moe_route_topk; both NULL: only
+ *            the logits are computed); err_word as moe_route_topk.
+ * Argument errors return a status code before anything is enqueued. */
+moe_status_t moe_router_topk(const void* x, const void* w_router, int dtype, int T, int d, int E,
+                             int k, int score, int normalize, float* logits, int32_t* topk_idx,
+                             float* topk_w, int32_t* err_word, void* stream);
+
+/* Backward of the router's map (same reading), given d_logits [T, E] float32
+ * (moe_route_topk_bwd's output):
+ *   d_w_router [E, d] float32 (out, nullable): sum over tokens of
+ *              d_logits[t, e] x[t], summed in token order (added to the
+ *              existing values when `accumulate`);
+ *   dx         [T, d] bf16 (in/out, nullable): dx[t] += sum_e d_logits[t, e]
+ *              w_router[e], the router's share of the layer's input gradient,
+ *              summed in float32 over experts in order and rounded once.
+ * x, w_router as moe_router_topk; d at most 2^20.  Both sums are taken in a
+ * fixed order (no atomics): the same inputs give the same bits. */
+moe_status_t moe_router_bwd(const void* x, const void* w_router, int dtype, const float* d_logits,
+                            int T, int d, int E, float* d_w_router, int accumulate, void* dx,
+                            void* stream);
+
 /* ---------------------------------------------------------------- permute
  * a2.  Expert-contiguous layout [P2 "主張と根拠"; P1 "ホストとデバイスの同期…"].
  * The row of assignment i = t*k + j (expert e) is

@@ -74,6 +74,10 @@ _SIGS = {
                                c_void_p, c_void_p]),
     "moe_route_topk_bwd": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                    c_int, c_void_p, c_void_p]),
+    "moe_router_topk": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_router_bwd": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int,
+                               c_void_p, c_int, c_void_p, c_void_p]),
     "moe_permute_workspace_size": (c_size_t, [c_int, c_int, c_int]),
     "moe_permute": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int, c_void_p,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,

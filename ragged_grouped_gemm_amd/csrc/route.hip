@@ -11,6 +11,7 @@
 // the lower id first among equal logits.  The logits row is only E floats, so
 // the kernel is latency-bound and tiny next to the GEMMs.
 #include "common.hpp"
+#include "route.hpp"
 
 #include <math.h>
 
@@ -30,8 +31,6 @@ int device_cu_count() {
   return cached[dev];
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
-
 template <int MAXK>
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int score, int normalize,
@@ -40,77 +39,8 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
                                                          int32_t* err_word) {
   int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float bv[MAXK];
-  int bi[MAXK];
-#pragma unroll
-  for (int p = 0; p < MAXK; ++p) {
-    bv[p] = -INFINITY;
-    bi[p] = -1;
-  }
-  bool nan_seen = false;
-  for (int e = 0; e < E; ++e) {
-    float v = row[e];
-    if (v != v) {
-      nan_seen = true;
-      v = -INFINITY;
-    }
-    int id = e;
-#pragma unroll
-    for (int p = 0; p < MAXK; ++p) {
-      // (v, id) beats the entry when its logit is larger, or equal with a lower
-      // id (a displaced entry carried down the list may tie a later entry)
-      bool take = (p < k) && (bi[p] < 0 || v > bv[p] || (v == bv[p] && id >= 0 && id < bi[p]));
-      float tv = bv[p];
-      int ti = bi[p];
-      bv[p] = take ? v : tv;
-      bi[p] = take ? id : ti;
-      v = take ? tv : v;
-      id = take ? ti : id;
-    }
-  }
-  if (nan_seen) set_err(err_word, MOE_ERRBIT_NAN_LOGIT);
-
-  float g[MAXK];
-  float s = 0.0f;
-  if (score == MOE_SCORE_SOFTMAX) {
-    float m = bv[0];
-    if (normalize) {
-#pragma unroll
-      for (int p = 0; p < MAXK; ++p)
-        if (p < k) {
-          g[p] = expf(bv[p] - m);
-          s += g[p];
-        }
-    } else {
-      float mall = -INFINITY;
-      for (int e = 0; e < E; ++e) {
-        float v = row[e];
-        if (v == v) mall = fmaxf(mall, v);
-      }
-      for (int e = 0; e < E; ++e) {
-        float v = row[e];
-        if (v == v) s += expf(v - mall);
-      }
-#pragma unroll
-      for (int p = 0; p < MAXK; ++p)
-        if (p < k) g[p] = expf(bv[p] - mall);
-    }
-  } else {
-#pragma unroll
-    for (int p = 0; p < MAXK; ++p)
-      if (p < k) {
-        g[p] = sigmoidf_(bv[p]);
-        s += g[p];
-      }
-    if (!normalize) s = 1.0f;
-  }
-#pragma unroll
-  for (int p = 0; p < MAXK; ++p)
-    if (p < k) {
-      idx[(size_t)t * k + p] = bi[p];
-      w[(size_t)t * k + p] = (score == MOE_SCORE_SOFTMAX || normalize) ? g[p] / s : g[p];
-    }
+  route_select<MAXK>(logits + (size_t)t * E, E, k, score, normalize, idx + (size_t)t * k,
+                     w + (size_t)t * k, err_word);
 }
 
 template <int MAXK>
@@ -185,7 +115,7 @@ __global__ void __launch_bounds__(256) route_topk_bwd_kernel(
 #pragma unroll
     for (int p = 0; p < MAXK; ++p)
       if (p < k) {
-        gv[p] = sigmoidf_(lv[p]);
+        gv[p] = route_sigmoid(lv[p]);
         S += gv[p];
       }
     if (normalize) {

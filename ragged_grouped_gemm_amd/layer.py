@@ -32,6 +32,13 @@ as usual.  Between the passes the layer then needs only the routing, Y and
 its inputs, at the price of one more FC1 GEMM (4·R·d·f FLOP) per backward;
 the gradients are bit-identical to the stored-H path.
 
+Fused router (``router=True``, bf16 input): the layer computes its own
+logits as the router's linear map x w_router^T, fused with the top-k routing
+in one launch (``moe_router_topk``); pass the router weight w_router [E, d]
+where the logits would go (forward, backward, step, capture).  The backward
+adds the router's share dlogits w_router to dX and writes its weight
+gradient ``dWr`` [E, d] (float32, ``moe_router_bwd``).
+
 MXFP8 variant (``gemm="mxfp8"``; ``gemm="mxfp4"`` is the same with E2M1
 elements; ``mx_dxp=True`` also writes FC1's dgrad output dXp as an MX row
 copy and sums dX from it): every GEMM operand is an MXFP8 copy blocked
@@ -77,7 +84,8 @@ class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
-                 recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=True):
+                 recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=True,
+                 router=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
             raise ValueError(gemm)
@@ -94,6 +102,9 @@ class MoEFFN:
         self.x_saved = None
         if self.mx and (bias or act == "srelu" or dtype != torch.bfloat16):
             raise ValueError("the MXFP8 variant is gated, bias-free, with bf16 activations")
+        if router and dtype != torch.bfloat16:
+            raise ValueError("the fused router takes a bf16 input")
+        self.router = router
         self.R = R = T * k
         self.dtype, self.act, self.score, self.normalize = dtype, act, score, normalize
         self.clamp, self.alpha, self.gelu_tanh = clamp, alpha, gelu_tanh
@@ -114,6 +125,8 @@ class MoEFFN:
         self.src_row = z((R,), i32)
         self.ws = z((ops.moe_permute_workspace_size(T, E, k),), torch.uint8)
         self.has_backward = backward
+        self.logits = z((T, E), f32) if router else None
+        self.dWr = z((E, d), f32) if router and backward else None
         self.timer = None          # optional OpTimer: HIP events around each library call
         if self.mx:
             self._alloc_mx(z, dev)
@@ -176,18 +189,42 @@ class MoEFFN:
     def _op(self, name):
         return self.timer.op(name) if self.timer is not None else contextlib.nullcontext()
 
+    def _route(self, x, logits):
+        """Top-k routing of the given logits, or (fused router) of x w_router^T
+        with ``logits`` the router weight."""
+        if self.router:
+            with self._op("router_topk"):
+                ops.moe_router_topk(x, logits, self.k, self.score, self.normalize,
+                                    logits=self.logits, topk_idx=self.topk_idx,
+                                    topk_w=self.topk_w, err_word=self.err)
+            self.x_saved = x
+        else:
+            with self._op("route_topk"):
+                ops.moe_route_topk(logits, self.k, self.score, self.normalize, self.topk_idx,
+                                   self.topk_w, self.err)
+
+    def _route_bwd(self, logits):
+        with self._op("route_topk_bwd"):
+            ops.moe_route_topk_bwd(self.logits if self.router else logits, self.topk_idx,
+                                   self.dgate, self.score, self.normalize, d_logits=self.dlogits)
+
+    def _router_bwd(self, logits):
+        """The router's share of dX and its weight gradient (after dX is written)."""
+        if self.router:
+            with self._op("router_bwd"):
+                ops.moe_router_bwd(self.x_saved, logits, self.dlogits, d_w_router=self.dWr,
+                                   dx=self.dX)
+
     def forward(self, x, logits, W1p, W2, b1p=None, b2=None):
         if self.mx:
             return self._forward_mx(x, logits, W1p)
-        with self._op("route_topk"):
-            ops.moe_route_topk(logits, self.k, self.score, self.normalize, self.topk_idx,
-                               self.topk_w, self.err)
+        self._route(x, logits)
         fused = self.fuse_permute
         with self._op("permute"):
             ops.moe_permute(x, self.topk_idx, self.E, counts=self.counts, offsets=self.offsets,
                             row_map=self.row_map, src_row=self.src_row, xp=self.xp, ws=self.ws,
                             err_word=self.err, gather=not fused)
-        self.x_saved = x if fused else None
+        self.x_saved = x if (fused or self.router) else None
         self.b1p_saved = b1p
         with self._op("fc1_glu_fwd"):
             self._fc1(x, W1p, b1p, save_h=self.H is not None and not self.recompute)
@@ -218,9 +255,7 @@ class MoEFFN:
         with self._op("combine_bwd"):
             ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w, d_y=self.dY,
                                           d_topk_w=self.dgate)
-        with self._op("route_topk_bwd"):
-            ops.moe_route_topk_bwd(logits, self.topk_idx, self.dgate, self.score,
-                                   self.normalize, d_logits=self.dlogits)
+        self._route_bwd(logits)
         if self.W2t is not None:
             with self._op("transpose_w2"):
                 ops.moe_transpose_weights(W2, self.W2t)
@@ -249,13 +284,12 @@ class MoEFFN:
                                          out=self.dW1p, db=self.db1p, max_cus=self.max_cus)
         with self._op("unpermute_dx"):
             ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
+        self._router_bwd(logits)
         return self.dX
 
     def _forward_mx(self, x, logits, W: MXWeights):
         E, R, f, d = self.E, self.R, self.f, self.d
-        with self._op("route_topk"):
-            ops.moe_route_topk(logits, self.k, self.score, self.normalize, self.topk_idx,
-                               self.topk_w, self.err)
+        self._route(x, logits)
         with self._op("permute"):
             ops.moe_permute(x, self.topk_idx, E, counts=self.counts, offsets=self.offsets,
                             pad_offsets=self.pad_offsets, row_map=self.row_map,
@@ -283,9 +317,7 @@ class MoEFFN:
         with self._op("combine_bwd"):
             ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w,
                                           d_topk_w=self.dgate, want_dy=False)
-        with self._op("route_topk_bwd"):
-            ops.moe_route_topk_bwd(logits, self.topk_idx, self.dgate, self.score,
-                                   self.normalize, d_logits=self.dlogits)
+        self._route_bwd(logits)
         with self._op("quantize_dy"):
             ops.moe_mx_quantize_experts(d_out, self.offsets, self.pad_offsets, R,
                                         src_row=self.src_row, row_map=self.row_map,
@@ -317,6 +349,7 @@ class MoEFFN:
                 ops.moe_unpermute_combine_mx(self.dXp, self.row_map, None, out=self.dX)
             else:
                 ops.moe_unpermute_combine(self.dXp, self.row_map, None, out=self.dX)
+        self._router_bwd(logits)
         return self.dX
 
     def step(self, x, logits, W1p, W2, d_out, b1p=None, b2=None):

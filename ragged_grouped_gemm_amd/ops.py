@@ -162,6 +162,42 @@ def moe_route_topk_bwd(logits, topk_idx, d_topk_w, score="softmax", normalize=Tr
     return d_logits
 
 
+def moe_router_topk(x, w_router, k, score="softmax", normalize=True, logits=None, topk_idx=None,
+                    topk_w=None, err_word=None, want_logits=True, route=True):
+    """The router's logits x w_router^T with the top-k routing of the same
+    launch.  Returns (logits or None, topk_idx or None, topk_w or None)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != d:
+        raise ValueError("w_router must be [E, d]")
+    if want_logits and logits is None:
+        logits = _empty((T, E), torch.float32, x)
+    if route:
+        topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+        topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    else:
+        topk_idx = topk_w = None
+    check(_lib.load().moe_router_topk(_p(x), _p(w_router), _dtype(x), T, d, E, k, SCORE[score],
+                                      int(normalize), _p(logits), _p(topk_idx), _p(topk_w),
+                                      _p(err_word), _stream()),
+          "moe_router_topk")
+    return logits, topk_idx, topk_w
+
+
+def moe_router_bwd(x, w_router, d_logits, d_w_router=None, want_dw=True, accumulate=False,
+                   dx=None):
+    """d_w_router = d_logits^T x (float32) and dx += d_logits w_router (dx bf16,
+    in place, when given).  Returns d_w_router."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    if want_dw and d_w_router is None:
+        d_w_router = _empty((E, d), torch.float32, x)
+    check(_lib.load().moe_router_bwd(_p(x), _p(w_router), _dtype(x), _p(d_logits), T, d, E,
+                                     _p(d_w_router), int(accumulate), _p(dx), _stream()),
+          "moe_router_bwd")
+    return d_w_router
+
+
 def moe_permute_workspace_size(T, E, k) -> int:
     return int(_lib.load().moe_permute_workspace_size(T, E, k))
 

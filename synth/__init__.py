@@ -32,7 +32,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "MoEConfig", "WORKLOADS", "workload", "make_inputs", "f32_to_bf16_bits",
+    "MoEConfig", "WORKLOADS", "workload", "make_inputs", "f32_to_bf16_bits", "draw_router_weights",
     "bf16_bits_to_f32", "draw_router", "to_torch",
 ]
 
@@ -155,6 +155,13 @@ def draw_router(cfg: MoEConfig, T: Optional[int] = None) -> np.ndarray:
         bias[empty] = -30.0
     z = np.random.default_rng([cfg.seed, 1]).standard_normal((T, E), dtype=np.float32)
     return (z + bias).astype(np.float32)
+
+
+def draw_router_weights(cfg: MoEConfig) -> np.ndarray:
+    """Router weight [E, d] ~ N(0, 1/d) as bf16 bits (for layers that compute
+    their own logits from x)."""
+    a = _normal(np.random.default_rng([cfg.seed, 6]), (cfg.E, cfg.d), 1.0 / math.sqrt(cfg.d))
+    return f32_to_bf16_bits(a)
 
 
 def _normal(rng, shape, scale=1.0):

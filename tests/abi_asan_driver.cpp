@@ -101,6 +101,28 @@ int main(int argc, char** argv) {
   EXPECT(moe_route_topk_bwd(PF, nullptr, PF, 4, 8, 2, 0, 1, PF, nullptr) == MOE_ERR_INVALID_ARG);
   EXPECT(moe_route_topk_bwd(PF, PI, PF, 4, 8, 9, 0, 1, PF, nullptr) == MOE_ERR_INVALID_ARG);
 
+  // ---- fused router
+  EXPECT(moe_router_topk(P, P, MOE_F32, 4, 64, 8, 2, 0, 1, PF, PI, PF, nullptr, nullptr) ==
+         MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_router_topk(P, P, 9, 4, 64, 8, 2, 0, 1, PF, PI, PF, nullptr, nullptr) ==
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_router_topk(P, P, MOE_BF16, 4, 48, 8, 2, 0, 1, PF, PI, PF, nullptr, nullptr) ==
+         MOE_ERR_INVALID_ARG);                                                   // d % 32
+  EXPECT(moe_router_topk(P, P, MOE_BF16, 4, 64, 8, 2, 0, 1, PF, PI, nullptr, nullptr, nullptr) ==
+         MOE_ERR_INVALID_ARG);                                                   // idx without w
+  EXPECT(moe_router_topk(P, P, MOE_BF16, 4, 64, 300, 2, 0, 1, nullptr, PI, PF, nullptr,
+                         nullptr) == MOE_ERR_INVALID_ARG);                       // E > 256: logits
+  EXPECT(moe_router_topk(P, P, MOE_BF16, 4, 64, 8, 9, 0, 1, PF, PI, PF, nullptr, nullptr) ==
+         MOE_ERR_INVALID_ARG);                                                   // k > E
+  EXPECT(moe_router_topk(nullptr, nullptr, MOE_BF16, 0, 64, 8, 2, 0, 1, PF, PI, PF, nullptr,
+                         nullptr) == MOE_OK);
+  EXPECT(moe_router_bwd(P, P, MOE_BF16, PF, 4, 40, 8, PF, 0, P, nullptr) == MOE_ERR_INVALID_ARG);
+  EXPECT(moe_router_bwd(P, P, MOE_BF16, PF, 4, (1 << 20) + 32, 8, PF, 0, P, nullptr) ==
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_router_bwd(nullptr, P, MOE_BF16, PF, 4, 64, 8, PF, 0, nullptr, nullptr) ==
+         MOE_ERR_INVALID_ARG);                                                   // dWr without x
+  EXPECT(moe_router_bwd(P, P, MOE_F32, PF, 4, 64, 8, PF, 0, P, nullptr) == MOE_ERR_UNSUPPORTED);
+
   // ---- permute (with and without a workspace)
   EXPECT(moe_permute(nullptr, MOE_BF16, 1000, 0, PI, 2, 8, PI, PI, nullptr, PI, PI, nullptr, P, 4,
                      nullptr, nullptr) == MOE_ERR_WORKSPACE);
