@@ -39,6 +39,13 @@ where the logits would go (forward, backward, step, capture).  The backward
 adds the router's share dlogits w_router to dX and writes its weight
 gradient ``dWr`` [E, d] (float32, ``moe_router_bwd``).
 
+Buffers (``alloc``): every buffer the layer holds is taken from
+``alloc(shape, dtype, device)`` when given (caller-managed memory, guard
+bands), else from ``torch.zeros``.  Their initial contents do not matter:
+each pass writes every element it later reads, the padding of the MX
+column copies included; the error word, whose bits are sticky, is cleared
+once here.
+
 MXFP8 variant (``gemm="mxfp8"``; ``gemm="mxfp4"`` is the same with E2M1
 elements; ``mx_dxp=True`` also writes FC1's dgrad output dXp as an MX row
 copy and sums dX from it): every GEMM operand is an MXFP8 copy blocked
@@ -85,7 +92,7 @@ class MoEFFN:
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
                  recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=True,
-                 router=False):
+                 router=False, alloc=None):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
             raise ValueError(gemm)
@@ -114,11 +121,18 @@ class MoEFFN:
         i32, f32 = torch.int32, torch.float32
 
         def z(shape, dt):
+            if alloc is not None:
+                t = alloc(tuple(shape), dt, dev)
+                same_dev = t.device.type == dev.type and dev.index in (None, t.device.index)
+                if tuple(t.shape) != tuple(shape) or t.dtype != dt or not same_dev:
+                    raise ValueError("alloc returned a tensor of another shape, type or device")
+                return t
             return torch.zeros(shape, dtype=dt, device=dev)
 
         self.topk_idx = z((T, k), i32)
         self.topk_w = z((T, k), f32)
         self.err = z((1,), i32)
+        self.err.zero_()           # the only buffer read before it is written (sticky bits)
         self.counts = z((E,), i32)
         self.offsets = z((E + 1,), i32)
         self.row_map = z((T, k), i32)

@@ -68,7 +68,7 @@ def _device_inputs(cfg, inp):
     return x, lg, W1p, W2, b1p, b2, dout
 
 
-def _layer(cfg, fused=False, recompute=False, transpose_w2=True, transpose_w1=False):
+def _layer(cfg, fused=False, recompute=False, transpose_w2=True, transpose_w1=True):
     from ragged_grouped_gemm_amd.layer import MoEFFN
     dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     return MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, dtype=dt, act=cfg.act, score=cfg.score,
