@@ -52,6 +52,14 @@ Readings of points the pages leave open (each is listed in the design doc):
    gradient passes where the raw value lies inside the closed interval.
  * alpha scales the sigmoid argument: silu_a(g) = g * sigmoid(a g).
  * b2 is added to each expert output before the gate weighting.
+ * Feature scaling ([P1 GLU]: the epilogues also scale): a per-row float32
+   factor s[r] multiplying the activation output, A[r] = s[r] * act(H[r]);
+   its gradient is ds[r] = sum over c of dA[r, c] * act(H[r])[c], and the
+   activation's input gradient is taken at s[r] * dA.  With the gates as the
+   factors (``LayerSpec(gate_in_act=True)``: s[r] = w[t, j] for the row r of
+   assignment (t, j)) the combine sums the expert outputs with unit weights
+   and the gate gradient is ds; a bias b2 is then added after the weighting
+   instead of before it.
  * MXFP8 operands ([P1 Quant]; format in ``oracle/mx.py``): every GEMM operand
    is quantized in blocks of 32 along that GEMM's reduction axis.  Row copies
    (blocks along features) feed the forward and dgrad GEMMs; column copies
@@ -388,6 +396,28 @@ def srelu_backward(dA, h, clamp: float = 0.0):
     return np.asarray(dA, dtype=np.float64) * act_grad(h, "srelu") * m
 
 
+def row_scale_forward(A, s):
+    """Feature scaling of the activation output: A[r] * s[r].  [P1 GLU]"""
+    return np.asarray(s, dtype=np.float64)[:, None] * np.asarray(A, dtype=np.float64)
+
+
+def row_scale_backward(dA, A, s):
+    """Backward of :func:`row_scale_forward` at the unscaled activation A:
+    (s[r] * dA[r], the gradient the activation receives;  ds[r] = <dA[r], A[r]>)."""
+    dA = np.asarray(dA, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    return np.asarray(s, dtype=np.float64)[:, None] * dA, (dA * A).sum(axis=1)
+
+
+def rows_of_assignments(v, row_map):
+    """v[t, j] moved to the row of assignment (t, j): out[row_map[t, j]] = v[t, j]."""
+    v = np.asarray(v, dtype=np.float64)
+    row_map = np.asarray(row_map, dtype=np.int64)
+    out = np.zeros(row_map.size)
+    out[row_map.reshape(-1)] = v.reshape(-1)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Grouped GEMMs over the ragged expert segments  [P2 "主張と根拠"; P1 Sync]
 
@@ -505,7 +535,8 @@ class LayerSpec:
     """Options of the layer (what the configs vary)."""
 
     def __init__(self, k, score="softmax", normalize=True, act="swiglu", clamp=0.0,
-                 alpha=1.0, gelu_tanh=False, store="bf16", gemm="bf16", mx_dxp=False):
+                 alpha=1.0, gelu_tanh=False, store="bf16", gemm="bf16", mx_dxp=False,
+                 gate_in_act=False):
         self.k = k
         self.score = score
         self.normalize = normalize
@@ -520,6 +551,9 @@ class LayerSpec:
         # along d, from the exact values) instead of bf16, as for a quantized
         # backward dispatch; the unpermute-sum then adds the decoded rows
         self.mx_dxp = mx_dxp
+        # the gates scale FC1's activation output (feature scaling) and the
+        # combine sums with unit weights
+        self.gate_in_act = gate_in_act
 
     @property
     def gated(self):
@@ -561,8 +595,12 @@ def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
         A = glu_forward(H[:, :f], H[:, f:], spec.act, spec.clamp, spec.alpha, spec.gelu_tanh)
     else:
         A = srelu_forward(H, spec.clamp)
-    H_s = rnd(H)
     res = {}
+    if spec.gate_in_act:
+        w_row = rows_of_assignments(w, row_map)
+        res.update(w_row=w_row, A_unscaled=A)
+        A = row_scale_forward(A, w_row)
+    H_s = rnd(H)
     if q:
         # A from its exact values: row copy along f for FC2, column copy along
         # tokens for the FC2 weight gradient
@@ -576,7 +614,7 @@ def layer_forward(x, logits, W1, W2, b1=None, b2=None, *, spec: LayerSpec):
         A_s = A_fc2 = rnd(A)
     Y = grouped_linear(A_fc2, _mx.mx_qdq(_f64(W2), 2, fmt=spec.fmt) if q else W2, offsets, b2)
     Y_s = rnd(Y)
-    out = combine(Y_s, row_map, w)
+    out = combine(Y_s, row_map, None if spec.gate_in_act else w)
     res.update(topk_idx=idx, topk_w=w, nan=nan, counts=counts, offsets=offsets,
                row_map=row_map, src_row=src_row, xp=xp, H=H_s, A=A_s, Y=Y_s,
                out=rnd(out), H_exact=H, A_exact=A, Y_exact=Y, out_exact=out)
@@ -597,8 +635,12 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
     offsets, row_map = fwd["offsets"], fwd["row_map"]
     q = spec.mx
     dout = _f64(dout)
-    dY, dgate = combine_bwd(dout, fwd["Y"], row_map, fwd["topk_w"])
-    dlogits = route_topk_bwd(logits, fwd["topk_idx"], dgate, spec.score, spec.normalize)
+    T, k = row_map.shape
+    if spec.gate_in_act:
+        # unit-weight combine: every row of token t receives d_out[t]
+        dY, _ = combine_bwd(dout, fwd["Y"], row_map, np.ones((T, k)))
+    else:
+        dY, dgate = combine_bwd(dout, fwd["Y"], row_map, fwd["topk_w"])
     if q:
         pad = fwd["pad_offsets"]
         # dY from the product w * dOut: row copy along d (FC2 dgrad), column
@@ -612,13 +654,26 @@ def layer_backward(fwd: dict, dout, logits, W1, W2, *, spec: LayerSpec, has_bias
         dW2, db2 = grouped_wgrad(dY_s, fwd["A"], offsets, with_bias=True)
         dA = grouped_dgrad(dY_s, W2, offsets)
     H = fwd["H"]
+    dA_act = dA
+    if spec.gate_in_act:
+        # the gate gradient comes out of the activation's feature scaling, at
+        # the activation of the stored H (which the backward epilogue reads)
+        if spec.gated:
+            f = W1.shape[1] // 2
+            A_h = glu_forward(H[:, :f], H[:, f:], spec.act, spec.clamp, spec.alpha,
+                              spec.gelu_tanh)
+        else:
+            A_h = srelu_forward(H, spec.clamp)
+        dA_act, ds = row_scale_backward(dA, A_h, fwd["w_row"])
+        dgate = ds[row_map]
+    dlogits = route_topk_bwd(logits, fwd["topk_idx"], dgate, spec.score, spec.normalize)
     if spec.gated:
         f = W1.shape[1] // 2
-        dg, dl = glu_backward(dA, H[:, :f], H[:, f:], spec.act, spec.clamp, spec.alpha,
+        dg, dl = glu_backward(dA_act, H[:, :f], H[:, f:], spec.act, spec.clamp, spec.alpha,
                               spec.gelu_tanh)
         dH = np.concatenate([dg, dl], axis=1)
     else:
-        dH = srelu_backward(dA, H, spec.clamp)
+        dH = srelu_backward(dA_act, H, spec.clamp)
     if q:
         # dH from its exact values: row copy along 2f (FC1 dgrad; with f a
         # multiple of 32 its blocks are the same in packed and canonical
