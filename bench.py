@@ -60,6 +60,10 @@ def parse():
                     help="the layer computes its own logits: the router's map x w_router^T fused "
                          "with the top-k routing (w_router synthetic N(0, 1/d), so the routing is "
                          "not Zipf-skewed), and the router's backward (dWr, its share of dX)")
+    ap.add_argument("--gate-in-act", action="store_true",
+                    help="the routing gates scale FC1's activation output (feature scaling) "
+                         "and the combine sums with unit weights; the gate gradient comes "
+                         "from the dGLU epilogue, and the combine's backward does not read Y")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exit")
@@ -79,7 +83,7 @@ def gemm_flops(cfg):
     return fl
 
 
-def hbm_bytes(cfg, fused_permute=False):
+def hbm_bytes(cfg, fused_permute=False, gate_in_act=False):
     """Algorithmic bytes of the memory-bound kernels (each tensor read or written once)."""
     b = 4 if cfg.dtype == "f32" else 2
     T, R, d, k, E = cfg.T, cfg.R, cfg.d, cfg.k, cfg.E
@@ -105,6 +109,11 @@ def hbm_bytes(cfg, fused_permute=False):
         out.update({"combine_bwd": T * d * b + 2 * R * d * b + 12 * R,
                     "route_topk_bwd": T * E * 8 + T * k * 8,
                     "unpermute_dx": R * d * b + T * d * b + 4 * R})
+        if gate_in_act:
+            out["combine_bwd"] = T * d * b + R * d * b + 4 * R      # no Y, no gate gradient
+            out["gate_grad"] = 12 * R
+    if gate_in_act:
+        out["gates_to_rows"] = 12 * R
     return out
 
 
@@ -210,7 +219,7 @@ def main():
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
                recompute=args.recompute, mx_dxp=args.mx_dxp,
                transpose_w2=not args.no_transpose_w2, transpose_w1=not args.no_transpose_w1,
-               router=args.router)
+               router=args.router, gate_in_act=args.gate_in_act)
     if args.router:
         lg = t(synth.draw_router_weights(cfg))       # the layer's logits come from x lg^T
     permute = "fused" if L.fuse_permute else "copy"
@@ -248,7 +257,7 @@ def main():
         row = {"launches_per_step": n // args.steps, "ms": round(ms, 4)}
         if name in flops:
             row["tflops"] = round(flops[name] / ms / 1e9, 1)
-        hb = hbm_bytes(cfg, L.fuse_permute).get(name)
+        hb = hbm_bytes(cfg, L.fuse_permute, args.gate_in_act).get(name)
         if hb:
             row["gbs"] = round(hb / ms / 1e6, 1)
         kernels[name] = row
@@ -287,6 +296,7 @@ def main():
                    "permute": "mx_quantize_gather" if mx else permute,
                    "recompute_fc1": bool(args.recompute),
                    "fused_router": bool(args.router),
+                   "gate_in_act": bool(args.gate_in_act),
                    "mx_dxp": bool(args.mx_dxp),
                    "dgrad_weights_transposed": [n for n, on in
                                                 (("W2", not args.no_transpose_w2 and not mx),

@@ -249,6 +249,18 @@ moe_status_t moe_repack_glu_weights(const void* w, const float* b, int dtype, in
 moe_status_t moe_transpose_weights(const void* w, int dtype, int E, int rows, int cols, void* wt,
                                    void* stream);
 
+/* A float per assignment moved to the expert-contiguous row order and back
+ * (the routing gates as feature-scaling factors of FC1's activation, and
+ * their gradients) [P1 "融合された GEMM エピローグ…": feature scaling; P2
+ * "主張と根拠": the ragged expert-major layout]:
+ *   inverse == 0:  dst[row_map[i]] = src[i]
+ *   inverse == 1:  dst[i] = src[row_map[i]]          for i < n = T*k,
+ * row_map [T, k] from moe_permute (a permutation of [0, n)); src and dst
+ * [n] float32, distinct.  Entries of row_map outside [0, n) are skipped
+ * (forward) or give 0 (inverse).  Argument errors return a status code. */
+moe_status_t moe_permute_rows(const float* src, const int32_t* row_map, int n, int inverse,
+                              float* dst, void* stream);
+
 /* ---------------------------------------------------------------- grouped GEMMs
  * All grouped GEMMs run over the expert segments given by the DEVICE array
  * offsets [E+1] (offsets[0] = 0, nondecreasing, offsets[E] = R); segment e
@@ -301,6 +313,14 @@ typedef struct {
    * [0, src_rows) read as zeros. */
   const int32_t* src_row;
   int src_rows;
+  /* Feature scaling [P1 "融合された GEMM エピローグ…": the epilogues also
+   * scale] (nullable, every dtype): row_scale [R] float32, a factor per
+   * permuted row multiplying the activation output,
+   *   A[r] = row_scale[r] * act(...),
+   * applied to the float32 value before A is rounded or quantized.  With the
+   * routing gates as factors (moe_permute_rows) the combine then sums with
+   * unit weights. */
+  const float* row_scale;
 } moe_glu_fwd_args_t;
 moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* args, void* stream);
 
@@ -370,8 +390,26 @@ typedef struct {
    * w2t[e][j][i] == w2[e][i][j] (moe_transpose_weights).  When set it is read
    * instead of w2 (which may then be NULL), K-contiguous like dy. */
   const void* w2t;
+  /* Feature scaling (every dtype; see moe_glu_fwd_args_t.row_scale):
+   *   row_scale   [R] float32 (in, nullable): the activation's gradient is
+   *               taken at row_scale[r] * dA[r];
+   *   d_row_scale [R] float32 (out, nullable): the factor's gradient
+   *               ds[r] = sum_c dA[r,c] * act(H[r])[c]  (act of the stored H,
+   *               clamp included; unscaled dA), zero for rows at or past
+   *               offsets[E];
+   *   ws, ws_bytes: device workspace of at least
+   *               moe_glu_bwd_workspace_size(R, f) bytes, needed with
+   *               d_row_scale (else MOE_ERR_WORKSPACE): the epilogue writes
+   *               one partial sum per 32 columns of dA and row there, and a
+   *               second kernel adds them in column order (deterministic, no
+   *               atomics). */
+  const float* row_scale;
+  float* d_row_scale;
+  void* ws;
+  size_t ws_bytes;
 } moe_glu_bwd_args_t;
 moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* args, void* stream);
+size_t moe_glu_bwd_workspace_size(int R, int f);
 
 /* a9 / a10 / a11.  Backward of the grouped linear map y = a @ w[e]^T (+ b[e])
  * [P1 "融合された GEMM エピローグによる GLU 活性化関数の最適化": the backward
@@ -542,7 +580,9 @@ moe_status_t moe_unpermute_combine_mx(const moe_mx_t* y, int y_dtype, const int3
  *   d_topk_w[t,j]      = <d_out[t], y[row_map[t,j]]>   (float32, summed in a
  *                        fixed order)
  * d_out [T, d], y [T*k, d], d_y [T*k, d] dtype.  d_y or d_topk_w may be NULL
- * (an MXFP8 layer writes dY only as MXFP8 copies, with moe_mx_quantize_experts). */
+ * (an MXFP8 layer writes dY only as MXFP8 copies, with moe_mx_quantize_experts).
+ * topk_w NULL: unit weights (the combine of a layer whose gates scale FC1's
+ * activation); y is read only for d_topk_w and may be NULL without it. */
 moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dtype,
                                        const int32_t* row_map, const float* topk_w, int T,
                                        int k, int d, void* d_y, float* d_topk_w, void* stream);

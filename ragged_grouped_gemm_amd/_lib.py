@@ -38,7 +38,7 @@ class GluFwdArgs(ctypes.Structure):
                 ("alpha", c_float), ("gelu_tanh", c_int), ("h_out", c_void_p),
                 ("a_out", c_void_p), ("max_cus", c_int), ("xp_mx", _PMX), ("w1_mx", _PMX),
                 ("a_row", _PMX), ("a_col", _PMX), ("pad_offsets", c_void_p),
-                ("src_row", c_void_p), ("src_rows", c_int)]
+                ("src_row", c_void_p), ("src_rows", c_int), ("row_scale", c_void_p)]
 
 
 class GemmFwdArgs(ctypes.Structure):
@@ -54,7 +54,9 @@ class GluBwdArgs(ctypes.Structure):
                 ("d", c_int), ("f", c_int), ("act", c_int), ("clamp", c_float),
                 ("alpha", c_float), ("gelu_tanh", c_int), ("dh", c_void_p),
                 ("max_cus", c_int), ("dy_mx", _PMX), ("w2t_mx", _PMX), ("dh_row", _PMX),
-                ("dh_col", _PMX), ("pad_offsets", c_void_p), ("w2t", c_void_p)]
+                ("dh_col", _PMX), ("pad_offsets", c_void_p), ("w2t", c_void_p),
+                ("row_scale", c_void_p), ("d_row_scale", c_void_p), ("ws", c_void_p),
+                ("ws_bytes", c_size_t)]
 
 
 class GemmBwdArgs(ctypes.Structure):
@@ -85,6 +87,8 @@ _SIGS = {
     "moe_permute_noalloc": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_int,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p]),
+    "moe_permute_rows": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
+    "moe_glu_bwd_workspace_size": (c_size_t, [c_int, c_int]),
     "moe_repack_glu_weights": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                        c_void_p, c_void_p, c_void_p]),
     "moe_transpose_weights": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_void_p]),

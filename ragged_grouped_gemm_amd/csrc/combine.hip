@@ -52,15 +52,15 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
   for (int j = 0; j < k; ++j) {
     int r = row_map[(size_t)t * k + j];
     r = (r < 0 || r >= R) ? 0 : r;
-    float wj = w[(size_t)t * k + j];
+    const float wj = w ? w[(size_t)t * k + j] : 1.0f;
     float part = 0.0f;
     for (int c = lane; c < chunks; c += 64) {
       float g[V], v[V], o[V];
       unpack_chunk(dout[(size_t)t * chunks + c], g, EL());
-      unpack_chunk(y[(size_t)r * chunks + c], v, EL());
+      if (dw) unpack_chunk(y[(size_t)r * chunks + c], v, EL());
 #pragma unroll
       for (int q = 0; q < V; ++q) {
-        part = fmaf(g[q], v[q], part);
+        if (dw) part = fmaf(g[q], v[q], part);
         o[q] = wj * g[q];
       }
       if (dy) dy[(size_t)r * chunks + c] = pack_chunk(o, EL());
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel_k(
   for (int j = 0; j < K; ++j) {
     const int r = row_map[(size_t)t * K + j];
     rows[j] = (r < 0 || r >= R) ? 0 : r;
-    ws[j] = w[(size_t)t * K + j];
+    ws[j] = w ? w[(size_t)t * K + j] : 1.0f;
     part[j] = 0.0f;
   }
   for (int c = lane; c < chunks; c += 64) {
@@ -354,7 +354,8 @@ moe_status_t moe_unpermute_combine_bwd(const void* d_out, const void* y, int dty
                                        int k, int d, void* d_y, float* d_topk_w, void* stream) {
   MOE_CHECK_ARG(T >= 0 && k >= 1 && k <= MOE_MAX_TOPK && d > 0 && valid_dtype(dtype));
   if (T == 0) return MOE_OK;
-  MOE_CHECK_ARG(d_out && y && row_map && topk_w && (d_y || d_topk_w));
+  // unit weights when topk_w is NULL; y is read only for d_topk_w
+  MOE_CHECK_ARG(d_out && row_map && (d_y || d_topk_w) && (y || !d_topk_w));
   MOE_CHECK_ARG(aligned16(d_out) && aligned16(y) && aligned16(d_y));
   MOE_CHECK_ARG((d * dtype_size(dtype)) % 16 == 0);
   int chunks = (int)(d * dtype_size(dtype) / 16);

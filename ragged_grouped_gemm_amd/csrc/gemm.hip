@@ -142,6 +142,13 @@ struct GemmArgs {
   uint8_t* mxc_s;
   long long ld_mxc;
   const int32_t* pad_offsets;
+  // Feature scaling of the GLU / sReLU output (nullable): forward A[r] =
+  // row_scale[r] * act; backward the activation's gradient is taken at
+  // row_scale[r] * dA, and (ds_part non-null) each 32 x 32 block of dA adds
+  // its rows' sum of dA * act into ds_part[(col / 32) * ld_ds + r].
+  const float* row_scale;
+  float* ds_part;
+  long long ld_ds;
 };
 
 // ------------------------------------------------------------------ activations
@@ -594,7 +601,7 @@ template <int ACT, class S>
 __device__ __forceinline__ void epi_glu_fwd(S* __restrict__ Hrow, S* __restrict__ Arow,
                                             const float* __restrict__ bias,
                                             const f32x16& accg, const f32x16& accl, int c0,
-                                            int N, float L, float alpha, int gtanh) {
+                                            int N, float L, float alpha, int gtanh, float sc) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int col = c0 + 8 * g;
@@ -616,18 +623,28 @@ __device__ __forceinline__ void epi_glu_fwd(S* __restrict__ Hrow, S* __restrict_
         gt = fminf(gt, L);
         li = fminf(fmaxf(li, -L), L);
       }
-      o[q] = act_value<ACT>(gt, alpha, gtanh) * li;
+      o[q] = act_value<ACT>(gt, alpha, gtanh) * li * sc;
     }
     store4(Arow + (col >> 6) * 32 + (col & 31), o);
   }
 }
 
+// Feature-scaling gradient of one 32 x 32 block: the two lanes of a row
+// (l and l ^ 32) add their 16-value sums of dA * act, and the first writes
+// the block's partial for its row.  Both lanes of a row run this together.
+__device__ __forceinline__ void ds_block_store(float* __restrict__ ds_part, long long ld_ds,
+                                               int cblock, int row, bool live, float ps) {
+  const float tot = ps + __shfl_xor(ps, 32);
+  if (live && (threadIdx.x & 32) == 0) ds_part[(size_t)cblock * ld_ds + row] = tot;
+}
+
 // FC2 dgrad + dGLU: acc = dA at A columns c0 + ...; gate of A column c sits at
 // packed column 64 (c / 32) + c % 32 and the linear value 32 columns further.
+// sc: the row's feature scale; ps (in/out): the lane's sum of dA * act.
 template <int ACT, class S>
 __device__ __forceinline__ void epi_glu_bwd(const S* __restrict__ Hrow, S* __restrict__ Drow,
                                             const f32x16& acc, int c0, int N, float L,
-                                            float alpha, int gtanh) {
+                                            float alpha, int gtanh, float sc, float& ps) {
   float hg[4][4], hl[4][4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -655,7 +672,8 @@ __device__ __forceinline__ void epi_glu_bwd(const S* __restrict__ Hrow, S* __res
       }
       float a, da_dg;
       act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
-      const float d = acc[4 * g + q];
+      ps += acc[4 * g + q] * (a * li);
+      const float d = acc[4 * g + q] * sc;
       dg[q] = d * li * da_dg * mg;
       dl[q] = d * a * ml;
     }
@@ -669,7 +687,7 @@ __device__ __forceinline__ void epi_glu_bwd(const S* __restrict__ Hrow, S* __res
 template <int ACT>
 __device__ __forceinline__ void epi_glu_bwd_raw(const u32x2 (&h)[4][2], uint16_t* __restrict__ Drow,
                                                 const f32x16& acc, int c0, int N, float L,
-                                                float alpha, int gtanh) {
+                                                float alpha, int gtanh, float sc, float& ps) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int col = c0 + 8 * g;
@@ -690,7 +708,8 @@ __device__ __forceinline__ void epi_glu_bwd_raw(const u32x2 (&h)[4][2], uint16_t
       }
       float a, da_dg;
       act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
-      const float d = acc[4 * g + q];
+      ps += acc[4 * g + q] * (a * li);
+      const float d = acc[4 * g + q] * sc;
       dg[q] = d * li * da_dg * mg;
       dl[q] = d * a * ml;
     }
@@ -703,7 +722,7 @@ __device__ __forceinline__ void epi_glu_bwd_raw(const u32x2 (&h)[4][2], uint16_t
 template <class S>
 __device__ __forceinline__ void epi_srelu_fwd(S* __restrict__ Hrow, S* __restrict__ Arow,
                                               const float* __restrict__ bias, const f32x16& acc,
-                                              int c0, int N, float L) {
+                                              int c0, int N, float L, float sc) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int col = c0 + 8 * g;
@@ -714,7 +733,7 @@ __device__ __forceinline__ void epi_srelu_fwd(S* __restrict__ Hrow, S* __restric
       v[q] = acc[4 * g + q] + (bias ? bias[col + q] : 0.0f);
       const float h = L > 0.0f ? fminf(v[q], L) : v[q];
       const float r = fmaxf(h, 0.0f);
-      o[q] = r * r;
+      o[q] = r * r * sc;
     }
     if (Hrow) store4(Hrow + col, v);
     store4(Arow + col, o);
@@ -724,7 +743,8 @@ __device__ __forceinline__ void epi_srelu_fwd(S* __restrict__ Hrow, S* __restric
 // FC2 dgrad + squared-ReLU backward: dH = dA * 2 relu(h) * [h <= L].
 template <class S>
 __device__ __forceinline__ void epi_srelu_bwd(const S* __restrict__ Hrow, S* __restrict__ Drow,
-                                              const f32x16& acc, int c0, int N, float L) {
+                                              const f32x16& acc, int c0, int N, float L, float sc,
+                                              float& ps) {
   float hv[4][4];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
@@ -741,7 +761,9 @@ __device__ __forceinline__ void epi_srelu_bwd(const S* __restrict__ Hrow, S* __r
         m = h <= L ? 1.0f : 0.0f;
         h = fminf(h, L);
       }
-      o[q] = acc[4 * g + q] * 2.0f * fmaxf(h, 0.0f) * m;
+      const float r = fmaxf(h, 0.0f);
+      ps += acc[4 * g + q] * (r * r);
+      o[q] = acc[4 * g + q] * sc * 2.0f * r * m;
     }
     store4(Drow + col, o);
   }
@@ -820,7 +842,7 @@ __device__ __forceinline__ void mx_emit(const float* W, int lane, const GemmArgs
 template <int ACT>
 __device__ __forceinline__ void glu_fwd_values(uint16_t* __restrict__ Hrow, const f32x16& accg,
                                                const f32x16& accl, int c0, float L, float alpha,
-                                               int gtanh, bool rok, float* o) {
+                                               int gtanh, bool rok, float sc, float* o) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int col = c0 + 8 * g;
@@ -841,7 +863,7 @@ __device__ __forceinline__ void glu_fwd_values(uint16_t* __restrict__ Hrow, cons
         gt = fminf(gt, L);
         li = fminf(fmaxf(li, -L), L);
       }
-      o[4 * g + q] = rok ? act_value<ACT>(gt, alpha, gtanh) * li : 0.0f;
+      o[4 * g + q] = rok ? act_value<ACT>(gt, alpha, gtanh) * li * sc : 0.0f;
     }
   }
 }
@@ -865,7 +887,8 @@ __device__ __forceinline__ void glu_bwd_hload(const uint16_t* __restrict__ Hrow,
 template <int ACT>
 __device__ __forceinline__ void glu_bwd_values_h(const u32x2 (&h)[4][2], bool live,
                                                  const f32x16& acc, float L, float alpha,
-                                                 int gtanh, float* dg, float* dl) {
+                                                 int gtanh, float sc, float& ps, float* dg,
+                                                 float* dl) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     float hg[4], hl[4];
@@ -885,40 +908,9 @@ __device__ __forceinline__ void glu_bwd_values_h(const u32x2 (&h)[4][2], bool li
       }
       float a, da_dg;
       act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
-      const float d = live ? acc[4 * g + q] : 0.0f;
-      dg[4 * g + q] = d * li * da_dg * mg;
-      dl[4 * g + q] = d * a * ml;
-    }
-  }
-}
-
-// dGLU values of one dA block: gate and linear gradients (zero when Hrow is
-// null, i.e. for rows past the segment).
-template <int ACT>
-__device__ __forceinline__ void glu_bwd_values(const uint16_t* __restrict__ Hrow,
-                                               const f32x16& acc, int c0, float L, float alpha,
-                                               int gtanh, float* dg, float* dl) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int col = c0 + 8 * g;
-    const int pg = (col >> 5) * 64 + (col & 31);
-    float hg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (Hrow) {
-      load4(Hrow + pg, hg);
-      load4(Hrow + pg + 32, hl);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float gt = hg[q], li = hl[q], mg = 1.0f, ml = 1.0f;
-      if (L > 0.0f) {
-        mg = gt <= L ? 1.0f : 0.0f;
-        ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
-        gt = fminf(gt, L);
-        li = fminf(fmaxf(li, -L), L);
-      }
-      float a, da_dg;
-      act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
-      const float d = Hrow ? acc[4 * g + q] : 0.0f;
+      const float dr = live ? acc[4 * g + q] : 0.0f;
+      ps += dr * (a * li);
+      const float d = dr * sc;
       dg[4 * g + q] = d * li * da_dg * mg;
       dl[4 * g + q] = d * a * ml;
     }
@@ -1018,7 +1010,10 @@ struct GemmCfg {
   static_assert(!MX || BKB * EPB == 128, "MX steps are 128 k (four scale blocks, one word)");
 };
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false>
+// RS: the feature-scaling variant of a GLU / sReLU epilogue (row_scale,
+// ds_part); without it those fields are ignored and the code is the plain one.
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false,
+          bool RS = false>
 __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     grouped_gemm_kernel(GemmArgs p) {
   typedef GemmCfg<EL, EPI, TL> C;
@@ -1484,6 +1479,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         const int row = r0 + (lane & 31);
         const bool rok = row < mlim;
         const int prow = pe0 + (r0 - off_e);
+        const float sc = (RS && rok && p.row_scale) ? p.row_scale[row] : 1.0f;
         static_for<0, TN>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           const int cb = n0 + wn * C::WTN + 32 * j;
@@ -1495,7 +1491,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                     (rok && p.aux) ? reinterpret_cast<SO*>(p.aux) + (size_t)row * p.ld_aux
                                    : nullptr,
                     acc[i][j], acc[i][j + 1], cb + 4 * (lane >> 5), p.clamp, p.alpha,
-                    p.gelu_tanh, rok, o);
+                    p.gelu_tanh, rok, sc, o);
                 mx_stage(Wt, lane, o);
                 wave_lds_sync();
                 mx_emit<typename EL::Fmt>(Wt, lane, p, r0, mlim, (cb >> 6) * 32, prow, pe1);
@@ -1517,9 +1513,11 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                             cb2 + 4 * (lane >> 5), hbuf[(b + 1) & 1]);
             }
             if (cb < p.N) {
-              float dg[16], dl[16];
+              float dg[16], dl[16], ps = 0.0f;
               glu_bwd_values_h<epi_act(EPI)>(hbuf[b & 1], rok, acc[i][j], p.clamp, p.alpha,
-                                             p.gelu_tanh, dg, dl);
+                                             p.gelu_tanh, sc, ps, dg, dl);
+              if constexpr (RS)
+                if (p.ds_part) ds_block_store(p.ds_part, p.ld_ds, cb >> 5, row, rok, ps);
               const int pg0 = (cb >> 5) * 64;
               mx_stage(Wt, lane, dg);
               wave_lds_sync();
@@ -1564,10 +1562,16 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         const int row = m0 + wm * C::WTM + 32 * i + (lane & 31);
         if (row < mlim) {
           SO* Drow = reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc;
+          const float sc = (RS && p.row_scale) ? p.row_scale[row] : 1.0f;
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j) {
+            float ps = 0.0f;
             epi_glu_bwd_raw<epi_act(EPI)>(hr[i & 1][j], Drow, acc[i][j], cw + 32 * j, p.N,
-                                          p.clamp, p.alpha, p.gelu_tanh);
+                                          p.clamp, p.alpha, p.gelu_tanh, sc, ps);
+            const int cb = n0 + wn * C::WTN + 32 * j;
+            if constexpr (RS)
+              if (p.ds_part) ds_block_store(p.ds_part, p.ld_ds, cb >> 5, row, cb < p.N, ps);
+          }
         }
       });
     } else if (kStaged && !(GROUP == RAGGED_K && p.accumulate)) {
@@ -1649,21 +1653,29 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                   p.aux ? reinterpret_cast<SO*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
                   reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc,
                   p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], acc[i][j + 1],
-                  c0, p.N, p.clamp, p.alpha, p.gelu_tanh);
+                  c0, p.N, p.clamp, p.alpha, p.gelu_tanh,
+                  (RS && p.row_scale) ? p.row_scale[row] : 1.0f);
           } else if constexpr (epi_glu_bwd(EPI)) {
+            float ps = 0.0f;
             epi_glu_bwd<epi_act(EPI), SO>(
                 reinterpret_cast<const SO*>(p.aux) + (size_t)row * p.ld_aux,
                 reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0, p.N, p.clamp,
-                p.alpha, p.gelu_tanh);
+                p.alpha, p.gelu_tanh, (RS && p.row_scale) ? p.row_scale[row] : 1.0f, ps);
+            if constexpr (RS)
+              if (p.ds_part) ds_block_store(p.ds_part, p.ld_ds, c0 >> 5, row, c0 < p.N, ps);
           } else if constexpr (EPI == EPI_SRELU_FWD) {
             epi_srelu_fwd<SO>(
                 p.aux ? reinterpret_cast<SO*>(p.aux) + (size_t)row * p.ld_aux : nullptr,
                 reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc,
-                p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], c0, p.N, p.clamp);
+                p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr, acc[i][j], c0, p.N, p.clamp,
+                (RS && p.row_scale) ? p.row_scale[row] : 1.0f);
           } else if constexpr (EPI == EPI_SRELU_BWD) {
+            float ps = 0.0f;
             epi_srelu_bwd<SO>(reinterpret_cast<const SO*>(p.aux) + (size_t)row * p.ld_aux,
                              reinterpret_cast<SO*>(p.c) + (size_t)row * p.ldc, acc[i][j], c0,
-                             p.N, p.clamp);
+                             p.N, p.clamp, (RS && p.row_scale) ? p.row_scale[row] : 1.0f, ps);
+            if constexpr (RS)
+              if (p.ds_part) ds_block_store(p.ds_part, p.ld_ds, c0 >> 5, row, c0 < p.N, ps);
           }
         });
       }
@@ -1673,10 +1685,11 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
 
 // ------------------------------------------------------------------ launching
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false>
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, class TL, bool GATHER = false,
+          bool RS = false>
 moe_status_t launch_gemm(const GemmArgs& p, int max_cus, hipStream_t s) {
   typedef GemmCfg<EL, EPI, TL> C;
-  auto kern = grouped_gemm_kernel<EL, AKM, BKM, GROUP, EPI, TL, GATHER>;
+  auto kern = grouped_gemm_kernel<EL, AKM, BKM, GROUP, EPI, TL, GATHER, RS>;
   static int occ[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
@@ -1728,13 +1741,14 @@ inline int tile_variant() {
 #endif
 }
 
-template <class EL, bool AKM, bool BKM, int GROUP, int EPI, bool GATHER = false>
+template <class EL, bool AKM, bool BKM, int GROUP, int EPI, bool GATHER = false,
+          bool RS = false>
 moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
   if constexpr (sizeof(typename EL::storage) == 4) {
-    return launch_gemm<EL, AKM, BKM, GROUP, EPI, TF32, GATHER>(p, max_cus, s);
+    return launch_gemm<EL, AKM, BKM, GROUP, EPI, TF32, GATHER, RS>(p, max_cus, s);
   } else {
     constexpr bool kSweep =
-        !GATHER && (EPI == EPI_STORE || EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
+        !GATHER && !RS && (EPI == EPI_STORE || EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD);
     if constexpr (kSweep) {
       switch (tile_variant()) {
         case 0: return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig>(p, max_cus, s);
@@ -1745,12 +1759,12 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
         default: break;
       }
     }
-    if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall, GATHER>(p, max_cus, s);
+    if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall, GATHER, RS>(p, max_cus, s);
     if constexpr (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))
-      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu, GATHER>(p, max_cus, s);
+      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu, GATHER, RS>(p, max_cus, s);
     else if constexpr (!BKM)
-      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigPingPong, GATHER>(p, max_cus, s);
-    else return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig, GATHER>(p, max_cus, s);
+      return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigPingPong, GATHER, RS>(p, max_cus, s);
+    else return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBig, GATHER, RS>(p, max_cus, s);
   }
 }
 
@@ -1762,34 +1776,53 @@ typedef Tile<128, 128, 2, 2, 128, 2> TMxSmall;
 typedef Tile<256, 256, 2, 4, 64, 3, 1> TMx4Big;
 typedef Tile<128, 128, 2, 2, 64, 3> TMx4Small;
 
-template <int GROUP, int EPI>
+template <int GROUP, int EPI, bool RS = false>
 moe_status_t dispatch_mx(const GemmArgs& p, bool big, int max_cus, hipStream_t s, int dtype) {
   if (dtype == MOE_E2M1) {
-    if (big) return launch_gemm<MX4, true, true, GROUP, EPI, TMx4Big>(p, max_cus, s);
-    return launch_gemm<MX4, true, true, GROUP, EPI, TMx4Small>(p, max_cus, s);
+    if (big) return launch_gemm<MX4, true, true, GROUP, EPI, TMx4Big, false, RS>(p, max_cus, s);
+    return launch_gemm<MX4, true, true, GROUP, EPI, TMx4Small, false, RS>(p, max_cus, s);
   }
-  if (big) return launch_gemm<MX8, true, true, GROUP, EPI, TMxBig>(p, max_cus, s);
-  return launch_gemm<MX8, true, true, GROUP, EPI, TMxSmall>(p, max_cus, s);
+  if (big) return launch_gemm<MX8, true, true, GROUP, EPI, TMxBig, false, RS>(p, max_cus, s);
+  return launch_gemm<MX8, true, true, GROUP, EPI, TMxSmall, false, RS>(p, max_cus, s);
+}
+
+// The feature-scaling variant when row_scale or ds_part is set.
+template <int GROUP, int EPI>
+moe_status_t dispatch_mx_rs(const GemmArgs& p, bool big, int max_cus, hipStream_t s, int dtype) {
+  if (p.row_scale || p.ds_part) return dispatch_mx<GROUP, EPI, true>(p, big, max_cus, s, dtype);
+  return dispatch_mx<GROUP, EPI>(p, big, max_cus, s, dtype);
 }
 
 // p.gather selects the gather-fused loaders, built for FC1's forward (rows
 // of A) and the weight gradient (k-rows of B) only.
-template <bool AKM, bool BKM, int GROUP, int EPI>
-moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
+template <bool AKM, bool BKM, int GROUP, int EPI, bool RS = false>
+moe_status_t dispatch_rs(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
   constexpr bool kGather =
       (GROUP == RAGGED_M && AKM && (epi_glu_fwd(EPI) || EPI == EPI_SRELU_FWD)) ||
       (GROUP == RAGGED_K && !BKM && EPI == EPI_STORE);
   if constexpr (kGather) {
     if (p.gather) {
       if (dtype == MOE_BF16)
-        return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI, true>(p, big, max_cus, s);
-      return dispatch_tiles<F32, AKM, BKM, GROUP, EPI, true>(p, big, max_cus, s);
+        return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI, true, RS>(p, big, max_cus, s);
+      return dispatch_tiles<F32, AKM, BKM, GROUP, EPI, true, RS>(p, big, max_cus, s);
     }
   } else {
     if (p.gather) return MOE_ERR_UNSUPPORTED;
   }
-  if (dtype == MOE_BF16) return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
-  return dispatch_tiles<F32, AKM, BKM, GROUP, EPI>(p, big, max_cus, s);
+  if (dtype == MOE_BF16)
+    return dispatch_tiles<BF16, AKM, BKM, GROUP, EPI, false, RS>(p, big, max_cus, s);
+  return dispatch_tiles<F32, AKM, BKM, GROUP, EPI, false, RS>(p, big, max_cus, s);
+}
+
+// Plain epilogues ignore the feature-scaling fields; the GLU / sReLU ones take
+// their feature-scaling variant when row_scale or ds_part is set.
+template <bool AKM, bool BKM, int GROUP, int EPI>
+moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
+  if constexpr (EPI != EPI_STORE) {
+    if (p.row_scale || p.ds_part)
+      return dispatch_rs<AKM, BKM, GROUP, EPI, true>(dtype, p, big, max_cus, s);
+  }
+  return dispatch_rs<AKM, BKM, GROUP, EPI>(dtype, p, big, max_cus, s);
 }
 
 // Band height 4 and the weight gradients' alternating tile order.  (A
@@ -1849,6 +1882,51 @@ inline const void* ptr_field(const A* a, const void* const A::*f) {
   const size_t end = (size_t)(reinterpret_cast<const char*>(&(a->*f)) -
                               reinterpret_cast<const char*>(a)) + sizeof(const void*);
   return a->struct_size >= end ? a->*f : nullptr;
+}
+// A field appended to an argument struct: its value when struct_size covers
+// it, else zero (callers built against an older header).
+template <class A, class T>
+inline T opt_field(const A* a, T A::*f) {
+  const size_t end = (size_t)(reinterpret_cast<const char*>(&(a->*f)) -
+                              reinterpret_cast<const char*>(a)) + sizeof(T);
+  return a->struct_size >= end ? a->*f : T{};
+}
+
+// Feature-scaling gradient: ds[r] = sum over the 32-column blocks b, in
+// order, of part[b * R + r] for rows below offsets[E]; zero past it.
+__global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict__ part, int nb,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int E, int R, float* __restrict__ ds) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  float v = 0.0f;
+  if (r < offsets[E])
+    for (int b = 0; b < nb; ++b) v += part[(size_t)b * R + r];
+  ds[r] = v;
+}
+
+// Sets the feature-scaling fields of p from a glu_bwd argument struct;
+// returns the d_row_scale output (nullable) or an argument error.
+inline moe_status_t set_row_scale_bwd(GemmArgs& p, const moe_glu_bwd_args_t* a, float** ds) {
+  p.row_scale = opt_field(a, &moe_glu_bwd_args_t::row_scale);
+  *ds = opt_field(a, &moe_glu_bwd_args_t::d_row_scale);
+  if (*ds) {
+    void* ws = opt_field(a, &moe_glu_bwd_args_t::ws);
+    if (!ws || opt_field(a, &moe_glu_bwd_args_t::ws_bytes) <
+                   moe_glu_bwd_workspace_size(a->R, a->f))
+      return MOE_ERR_WORKSPACE;
+    p.ds_part = static_cast<float*>(ws);
+    p.ld_ds = a->R;
+  }
+  return MOE_OK;
+}
+
+// After the dGLU GEMM on the same stream: the rows' sums of the partials.
+inline moe_status_t ds_reduce(const GemmArgs& p, int f, float* ds, hipStream_t s) {
+  if (!ds) return MOE_OK;
+  hipLaunchKernelGGL(ds_reduce_kernel, dim3((p.R + 255) / 256), dim3(256), 0, s, p.ds_part,
+                     f / 32, p.offsets, p.E, p.R, ds);
+  return launch_status();
 }
 // A gathered source [rows, cols] must be addressable by 31-bit byte offsets.
 inline bool gather_fits(long long rows, long long cols, int dtype) {
@@ -1924,10 +2002,11 @@ moe_status_t glu_fwd_mx(const moe_glu_fwd_args_t* a, hipStream_t s) {
   p.alpha = a->alpha;
   p.act = a->act;
   p.gelu_tanh = a->gelu_tanh;
+  p.row_scale = opt_field(a, &moe_glu_fwd_args_t::row_scale);
   const bool big = big_ragged_m(a->R, a->E, n1);
   if (a->act == MOE_ACT_SWIGLU)
-    return dispatch_mx<RAGGED_M, EPI_SWIGLU_FWD>(p, big, a->max_cus, s, dt);
-  return dispatch_mx<RAGGED_M, EPI_GEGLU_FWD>(p, big, a->max_cus, s, dt);
+    return dispatch_mx_rs<RAGGED_M, EPI_SWIGLU_FWD>(p, big, a->max_cus, s, dt);
+  return dispatch_mx_rs<RAGGED_M, EPI_GEGLU_FWD>(p, big, a->max_cus, s, dt);
 }
 
 moe_status_t gemm_fwd_mx(const moe_gemm_fwd_args_t* a, hipStream_t s) {
@@ -1955,7 +2034,7 @@ moe_status_t gemm_fwd_mx(const moe_gemm_fwd_args_t* a, hipStream_t s) {
 
 moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
   const int dt = a->dtype;
-  MOE_CHECK_ARG(a->struct_size >= sizeof(moe_glu_bwd_args_t));
+  MOE_CHECK_ARG(a->struct_size >= offsetof(moe_glu_bwd_args_t, w2t));
   MOE_CHECK_ARG(a->act == MOE_ACT_SWIGLU || a->act == MOE_ACT_GEGLU);
   MOE_CHECK_ARG(a->d % 128 == 0);
   if (a->R == 0) return MOE_OK;
@@ -1980,10 +2059,13 @@ moe_status_t glu_bwd_mx(const moe_glu_bwd_args_t* a, hipStream_t s) {
   p.alpha = a->alpha;
   p.act = a->act;
   p.gelu_tanh = a->gelu_tanh;
+  float* ds = nullptr;
+  if (const moe_status_t st = set_row_scale_bwd(p, a, &ds); st != MOE_OK) return st;
   const bool big = big_ragged_m(a->R, a->E, a->f);
-  if (a->act == MOE_ACT_SWIGLU)
-    return dispatch_mx<RAGGED_M, EPI_SWIGLU_BWD>(p, big, a->max_cus, s, dt);
-  return dispatch_mx<RAGGED_M, EPI_GEGLU_BWD>(p, big, a->max_cus, s, dt);
+  const moe_status_t st = a->act == MOE_ACT_SWIGLU
+                              ? dispatch_mx_rs<RAGGED_M, EPI_SWIGLU_BWD>(p, big, a->max_cus, s, dt)
+                              : dispatch_mx_rs<RAGGED_M, EPI_GEGLU_BWD>(p, big, a->max_cus, s, dt);
+  return st != MOE_OK ? st : ds_reduce(p, a->f, ds, s);
 }
 
 moe_status_t gemm_bwd_mx(const moe_gemm_bwd_args_t* a, hipStream_t s) {
@@ -2074,6 +2156,7 @@ moe_status_t moe_grouped_gemm_glu_fwd(const moe_glu_fwd_args_t* a, void* stream)
     p.gather = g;
     p.gather_rows = a->src_rows;
   }
+  p.row_scale = opt_field(a, &moe_glu_fwd_args_t::row_scale);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool big = big_ragged_m(a->R, a->E, n1);
   if (a->act == MOE_ACT_SWIGLU)
@@ -2148,22 +2231,32 @@ moe_status_t moe_grouped_gemm_glu_bwd(const moe_glu_bwd_args_t* a, void* stream)
   p.alpha = a->alpha;
   p.act = a->act;
   p.gelu_tanh = a->gelu_tanh;
+  float* ds = nullptr;
+  if (const moe_status_t st = set_row_scale_bwd(p, a, &ds); st != MOE_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool big = big_ragged_m(a->R, a->E, a->f);
+  moe_status_t st;
   if (w2t) {
     p.b = w2t;        // [E][f][d]: N = f rows, K = d contiguous
     p.ldb = a->d;
     if (a->act == MOE_ACT_SWIGLU)
-      return dispatch<true, true, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
-    if (a->act == MOE_ACT_GEGLU)
-      return dispatch<true, true, RAGGED_M, EPI_GEGLU_BWD>(a->dtype, p, big, a->max_cus, s);
-    return dispatch<true, true, RAGGED_M, EPI_SRELU_BWD>(a->dtype, p, big, a->max_cus, s);
+      st = dispatch<true, true, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+    else if (a->act == MOE_ACT_GEGLU)
+      st = dispatch<true, true, RAGGED_M, EPI_GEGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+    else
+      st = dispatch<true, true, RAGGED_M, EPI_SRELU_BWD>(a->dtype, p, big, a->max_cus, s);
+  } else if (a->act == MOE_ACT_SWIGLU) {
+    st = dispatch<true, false, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+  } else if (a->act == MOE_ACT_GEGLU) {
+    st = dispatch<true, false, RAGGED_M, EPI_GEGLU_BWD>(a->dtype, p, big, a->max_cus, s);
+  } else {
+    st = dispatch<true, false, RAGGED_M, EPI_SRELU_BWD>(a->dtype, p, big, a->max_cus, s);
   }
-  if (a->act == MOE_ACT_SWIGLU)
-    return dispatch<true, false, RAGGED_M, EPI_SWIGLU_BWD>(a->dtype, p, big, a->max_cus, s);
-  if (a->act == MOE_ACT_GEGLU)
-    return dispatch<true, false, RAGGED_M, EPI_GEGLU_BWD>(a->dtype, p, big, a->max_cus, s);
-  return dispatch<true, false, RAGGED_M, EPI_SRELU_BWD>(a->dtype, p, big, a->max_cus, s);
+  return st != MOE_OK ? st : ds_reduce(p, a->f, ds, s);
+}
+
+size_t moe_glu_bwd_workspace_size(int R, int f) {
+  return R > 0 && f > 0 ? (size_t)((f + 31) / 32) * (size_t)R * sizeof(float) : 0;
 }
 
 moe_status_t moe_grouped_gemm_bwd(const moe_gemm_bwd_args_t* a, void* stream) {

@@ -228,6 +228,23 @@ std::mutex g_scratch_mu;
 int32_t* g_scratch[kMaxDevices];  // device address of `scratch` per device, once looked up
 
 // The current device's address of `scratch` (looked up on its first use).
+// A float per assignment to and from the expert-contiguous row order:
+// forward dst[row_map[i]] = src[i], inverse dst[i] = src[row_map[i]];
+// indices outside [0, n) are skipped (forward) or read as 0 (inverse).
+__global__ void __launch_bounds__(256) permute_rows_kernel(const float* __restrict__ src,
+                                                           const int32_t* __restrict__ row_map,
+                                                           int n, int inverse,
+                                                           float* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = row_map[i];
+  const bool ok = r >= 0 && r < n;
+  if (inverse)
+    dst[i] = ok ? src[r] : 0.0f;
+  else if (ok)
+    dst[r] = src[i];
+}
+
 moe_status_t scratch_on_current_device(int32_t** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
@@ -283,6 +300,16 @@ moe_status_t moe_permute_noalloc(const void* x, int dtype, int T, int d,
   if (st != MOE_OK) return st;
   return permute_run(x, dtype, T, d, topk_idx, k, E, counts, offsets, pad_offsets, row_map,
                      src_row, xp, ws, err_word, reinterpret_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_permute_rows(const float* src, const int32_t* row_map, int n, int inverse,
+                              float* dst, void* stream) {
+  MOE_CHECK_ARG(n >= 0 && (inverse == 0 || inverse == 1));
+  if (n == 0) return MOE_OK;
+  MOE_CHECK_ARG(src && row_map && dst && src != dst);
+  hipLaunchKernelGGL(permute_rows_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), src, row_map, n, inverse, dst);
+  return launch_status();
 }
 
 }  // extern "C"

@@ -39,6 +39,15 @@ where the logits would go (forward, backward, step, capture).  The backward
 adds the router's share dlogits w_router to dX and writes its weight
 gradient ``dWr`` [E, d] (float32, ``moe_router_bwd``).
 
+Gates inside the activation (``gate_in_act=True``): FC1's epilogue scales
+each row's activation output by its routing gate (feature scaling, gates
+moved to row order by ``moe_permute_rows``), the combine sums the expert
+outputs with unit weights, and the backward takes the gate gradient from the
+dGLU epilogue (sum over the row of dA * act) instead of from <dOut, Y>, so
+the combine's backward no longer reads Y.  Without b2 this is the same
+function as the default layer; with b2 the bias is added after the gate
+weighting.
+
 Buffers (``alloc``): every buffer the layer holds is taken from
 ``alloc(shape, dtype, device)`` when given (caller-managed memory, guard
 bands), else from ``torch.zeros``.  Their initial contents do not matter:
@@ -92,7 +101,7 @@ class MoEFFN:
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
                  recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=True,
-                 router=False, alloc=None):
+                 router=False, alloc=None, gate_in_act=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
             raise ValueError(gemm)
@@ -112,6 +121,7 @@ class MoEFFN:
         if router and dtype != torch.bfloat16:
             raise ValueError("the fused router takes a bf16 input")
         self.router = router
+        self.gate_in_act = gate_in_act
         self.R = R = T * k
         self.dtype, self.act, self.score, self.normalize = dtype, act, score, normalize
         self.clamp, self.alpha, self.gelu_tanh = clamp, alpha, gelu_tanh
@@ -142,6 +152,12 @@ class MoEFFN:
         self.logits = z((T, E), f32) if router else None
         self.dWr = z((E, d), f32) if router and backward else None
         self.timer = None          # optional OpTimer: HIP events around each library call
+        # gates as FC1's feature scaling: per-row gates, their gradient and the
+        # dGLU's partial sums
+        self.w_row = z((R,), f32) if gate_in_act else None
+        self.ds = z((R,), f32) if gate_in_act and backward else None
+        self.ds_ws = (z((max(ops.moe_glu_bwd_workspace_size(R, f), 1),), torch.uint8)
+                      if gate_in_act and backward else None)
         if self.mx:
             self._alloc_mx(z, dev)
             return
@@ -240,14 +256,30 @@ class MoEFFN:
                             err_word=self.err, gather=not fused)
         self.x_saved = x if (fused or self.router) else None
         self.b1p_saved = b1p
+        self._gates_to_rows()
         with self._op("fc1_glu_fwd"):
             self._fc1(x, W1p, b1p, save_h=self.H is not None and not self.recompute)
         with self._op("fc2_fwd"):
             ops.moe_grouped_gemm_fwd(self.A, W2, self.offsets, b=b2, y=self.Y,
                                      max_cus=self.max_cus)
         with self._op("combine"):
-            ops.moe_unpermute_combine(self.Y, self.row_map, self.topk_w, out=self.out)
+            ops.moe_unpermute_combine(self.Y, self.row_map, self._combine_w(), out=self.out)
         return self.out
+
+    def _gates_to_rows(self):
+        if self.gate_in_act:
+            with self._op("gates_to_rows"):
+                ops.moe_permute_rows(self.topk_w, self.row_map, out=self.w_row)
+
+    def _combine_w(self):
+        """Gates of the combine: unit weights when they scale FC1's activation."""
+        return None if self.gate_in_act else self.topk_w
+
+    def _gate_grad(self, logits):
+        """dgate from the dGLU's feature-scaling gradient, then the routing's backward."""
+        with self._op("gate_grad"):
+            ops.moe_permute_rows(self.ds, self.row_map, inverse=True, out=self.dgate)
+        self._route_bwd(logits)
 
     def _fc1(self, x, W1p, b1p, save_h):
         fused = self.fuse_permute
@@ -256,7 +288,8 @@ class MoEFFN:
                                      gelu_tanh=self.gelu_tanh, save_h=save_h,
                                      h_out=self.H if save_h else None, a_out=self.A,
                                      max_cus=self.max_cus,
-                                     src_row=self.src_row if fused else None)
+                                     src_row=self.src_row if fused else None,
+                                     row_scale=self.w_row)
 
     def backward(self, d_out, logits, W1p, W2):
         if not self.has_backward:
@@ -267,9 +300,14 @@ class MoEFFN:
             with self._op("fc1_recompute"):
                 self._fc1(self.x_saved, W1p, self.b1p_saved, save_h=True)
         with self._op("combine_bwd"):
-            ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w, d_y=self.dY,
-                                          d_topk_w=self.dgate)
-        self._route_bwd(logits)
+            if self.gate_in_act:
+                # unit weights: dY rows are d_out's, Y is not read
+                ops.moe_unpermute_combine_bwd(d_out, None, self.row_map, None, d_y=self.dY,
+                                              want_dgate=False)
+            else:
+                ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w,
+                                              d_y=self.dY, d_topk_w=self.dgate)
+                self._route_bwd(logits)
         if self.W2t is not None:
             with self._op("transpose_w2"):
                 ops.moe_transpose_weights(W2, self.W2t)
@@ -277,7 +315,10 @@ class MoEFFN:
             ops.moe_grouped_gemm_glu_bwd(self.dY, None if self.W2t is not None else W2, self.H,
                                          self.offsets, act=self.act, clamp=self.clamp,
                                          alpha=self.alpha, gelu_tanh=self.gelu_tanh, dh=self.dH,
-                                         max_cus=self.max_cus, w2t=self.W2t)
+                                         max_cus=self.max_cus, w2t=self.W2t,
+                                         row_scale=self.w_row, d_row_scale=self.ds, ws=self.ds_ws)
+        if self.gate_in_act:
+            self._gate_grad(logits)
         with self._op("fc2_wgrad"):
             ops.moe_grouped_gemm_bwd(self.dY, self.offsets, mode="wgrad", a=self.A, out=self.dW2,
                                      db=self.db2, max_cus=self.max_cus)
@@ -312,37 +353,43 @@ class MoEFFN:
             ops.moe_mx_quantize_experts(x, self.offsets, self.pad_offsets, R, src_row=self.src_row,
                                         row_out=self.xp_row, col_out=self.xp_col,
                                         want_col=self.has_backward)
+        self._gates_to_rows()
         with self._op("fc1_glu_fwd"):
             ops.moe_grouped_gemm_glu_fwd(self.xp_row, W.w1, self.offsets, E=E, f=f, act=self.act,
                                          clamp=self.clamp, alpha=self.alpha,
                                          gelu_tanh=self.gelu_tanh, h_out=self.H,
                                          pad_offsets=self.pad_offsets, a_row=self.A_row,
                                          a_col=self.A_col, want_col=self.has_backward,
-                                         max_cus=self.max_cus)
+                                         max_cus=self.max_cus, row_scale=self.w_row)
         with self._op("fc2_fwd"):
             ops.moe_grouped_gemm_fwd(self.A_row, W.w2, self.offsets, E=E, N=d, y=self.Y,
                                      max_cus=self.max_cus)
         with self._op("combine"):
-            ops.moe_unpermute_combine(self.Y, self.row_map, self.topk_w, out=self.out)
+            ops.moe_unpermute_combine(self.Y, self.row_map, self._combine_w(), out=self.out)
         return self.out
 
     def _backward_mx(self, d_out, logits, W: MXWeights):
         E, R, d = self.E, self.R, self.d
-        with self._op("combine_bwd"):
-            ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w,
-                                          d_topk_w=self.dgate, want_dy=False)
-        self._route_bwd(logits)
+        if not self.gate_in_act:
+            with self._op("combine_bwd"):
+                ops.moe_unpermute_combine_bwd(d_out, self.Y, self.row_map, self.topk_w,
+                                              d_topk_w=self.dgate, want_dy=False)
+            self._route_bwd(logits)
         with self._op("quantize_dy"):
             ops.moe_mx_quantize_experts(d_out, self.offsets, self.pad_offsets, R,
-                                        src_row=self.src_row, row_map=self.row_map,
-                                        topk_w=self.topk_w, row_out=self.dY_row,
+                                        src_row=self.src_row,
+                                        row_map=None if self.gate_in_act else self.row_map,
+                                        topk_w=self._combine_w(), row_out=self.dY_row,
                                         col_out=self.dY_col)
         with self._op("fc2_dgrad_dglu"):
             ops.moe_grouped_gemm_glu_bwd(self.dY_row, W.w2t, self.H, self.offsets, E=E,
                                          act=self.act, clamp=self.clamp, alpha=self.alpha,
                                          gelu_tanh=self.gelu_tanh, pad_offsets=self.pad_offsets,
                                          dh_row=self.dH_row, dh_col=self.dH_col,
-                                         max_cus=self.max_cus)
+                                         max_cus=self.max_cus, row_scale=self.w_row,
+                                         d_row_scale=self.ds, ws=self.ds_ws)
+        if self.gate_in_act:
+            self._gate_grad(logits)
         with self._op("fc2_wgrad"):
             ops.moe_grouped_gemm_bwd(self.dY_col, self.offsets, mode="wgrad", a=self.A_col,
                                      out=self.dW2, E=E, R=R, pad_offsets=self.pad_offsets,

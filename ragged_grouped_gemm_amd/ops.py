@@ -275,11 +275,12 @@ def moe_transpose_weights(w, wt=None):
 def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=0.0, alpha=1.0,
                              gelu_tanh=False, save_h=True, h_out=None, a_out=None, max_cus=0,
                              E=None, f=None, pad_offsets=None, a_row=None, a_col=None,
-                             want_row=True, want_col=True, src_row=None):
+                             want_row=True, want_col=True, src_row=None, row_scale=None):
     """FC1 + GLU epilogue.  Returns (A [R, f], H [R, n1] or None).
 
     src_row (gather-fused permute): xp is the unpermuted x [T, d] and row r
     of the product reads x[src_row[r]] (R = src_row.numel()).
+    row_scale (float32 [R], optional): feature scaling, A[r] = row_scale[r] * act.
     MXFP8 operands (xp, w1p MXTensor row copies along d; E and f given):
     returns ((A row copy, A column copy), H bf16)."""
     if isinstance(xp, MXTensor):
@@ -297,6 +298,7 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
                                _p(h_out) if save_h else None, None, max_cus, _mx(xp), _mx(w1p),
                                _mx(a_row if want_row else None),
                                _mx(a_col if want_col else None), _p(pad_offsets))
+        args.row_scale = _p(row_scale)
         check(_lib.load().moe_grouped_gemm_glu_fwd(ctypes.byref(args), _stream()),
               "moe_grouped_gemm_glu_fwd")
         return ((a_row if want_row else None), (a_col if want_col else None)), \
@@ -314,6 +316,7 @@ def moe_grouped_gemm_glu_fwd(xp, w1p, offsets, *, b1p=None, act="swiglu", clamp=
     if src_row is not None:
         args.src_row = _p(src_row)
         args.src_rows = T
+    args.row_scale = _p(row_scale)
     check(_lib.load().moe_grouped_gemm_glu_fwd(ctypes.byref(args), _stream()),
           "moe_grouped_gemm_glu_fwd")
     return a_out, (h_out if save_h else None)
@@ -345,11 +348,15 @@ def moe_grouped_gemm_fwd(a, w, offsets, *, b=None, y=None, max_cus=0, E=None, N=
 
 def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alpha=1.0,
                              gelu_tanh=False, dh=None, max_cus=0, E=None, pad_offsets=None,
-                             dh_row=None, dh_col=None, want_row=True, want_col=True, w2t=None):
+                             dh_row=None, dh_col=None, want_row=True, want_col=True, w2t=None,
+                             row_scale=None, d_row_scale=None, ws=None):
     """FC2 dgrad + dGLU epilogue -> dH [R, n1] (packed like h).
 
     w2t (bf16 / fp32, optional): W2 transposed [E, f, d] (moe_transpose_weights),
     read instead of w2 (which may then be None).
+    row_scale (float32 [R], optional): the forward's feature scaling;
+    d_row_scale (float32 [R], optional, written): its gradient, with the
+    partial sums in ws (allocated here when not given).
 
     MXFP8 operands (dy row copy along d, w2 the transposed copy [E*f, d]; E
     given; h bf16): returns (dH row copy, dH column copy)."""
@@ -366,6 +373,7 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
                                _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                                None, max_cus, _mx(dy), _mx(w2), _mx(dh_row if want_row else None),
                                _mx(dh_col if want_col else None), _p(pad_offsets))
+        _row_scale_bwd(args, R, f, row_scale, d_row_scale, ws, dev)
         check(_lib.load().moe_grouped_gemm_glu_bwd(ctypes.byref(args), _stream()),
               "moe_grouped_gemm_glu_bwd")
         return (dh_row if want_row else None), (dh_col if want_col else None)
@@ -381,9 +389,37 @@ def moe_grouped_gemm_glu_bwd(dy, w2, h, offsets, *, act="swiglu", clamp=0.0, alp
                            _p(offsets), E, R, d, f, ACT[act], clamp, alpha, int(gelu_tanh),
                            _p(dh), max_cus)
     args.w2t = _p(w2t)
+    _row_scale_bwd(args, R, f, row_scale, d_row_scale, ws, dy.device)
     check(_lib.load().moe_grouped_gemm_glu_bwd(ctypes.byref(args), _stream()),
           "moe_grouped_gemm_glu_bwd")
     return dh
+
+
+def moe_glu_bwd_workspace_size(R, f):
+    return int(_lib.load().moe_glu_bwd_workspace_size(R, f))
+
+
+def _row_scale_bwd(args, R, f, row_scale, d_row_scale, ws, dev):
+    args.row_scale = _p(row_scale)
+    if d_row_scale is not None:
+        nbytes = moe_glu_bwd_workspace_size(R, f)
+        if ws is None:
+            ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        args.d_row_scale = _p(d_row_scale)
+        args.ws = _p(ws)
+        args.ws_bytes = ws.numel() * ws.element_size()
+
+
+def moe_permute_rows(src, row_map, inverse=False, out=None):
+    """A float per assignment to the row order (out[row_map[i]] = src[i]) or,
+    with inverse, back (out[i] = src[row_map[i]]); src [T, k] or [T*k]."""
+    n = row_map.numel()
+    if out is None:
+        out = _empty(tuple(row_map.shape) if inverse else (n,), torch.float32, row_map)
+    check(_lib.load().moe_permute_rows(_p(src), _p(row_map), n, int(inverse), _p(out),
+                                       _stream()),
+          "moe_permute_rows")
+    return out
 
 
 def moe_grouped_gemm_bwd(g, offsets, *, mode, w=None, a=None, out=None, db=None, want_db=False,
@@ -477,13 +513,17 @@ def moe_unpermute_combine_mx(y_mx: MXTensor, row_map, topk_w=None, out=None,
     return out
 
 
-def moe_unpermute_combine_bwd(d_out, y, row_map, topk_w, d_y=None, d_topk_w=None, want_dy=True):
+def moe_unpermute_combine_bwd(d_out, y, row_map, topk_w, d_y=None, d_topk_w=None, want_dy=True,
+                              want_dgate=True):
+    """dY rows (topk_w None: unit weights) and the gate gradient (want_dgate;
+    y is read only for it and may be None without it)."""
     T, k = row_map.shape
-    d = y.shape[1]
+    d = d_out.shape[1]
     if want_dy and d_y is None:
-        d_y = torch.empty_like(y)
-    d_topk_w = _empty((T, k), torch.float32, y) if d_topk_w is None else d_topk_w
-    check(_lib.load().moe_unpermute_combine_bwd(_p(d_out), _p(y), _dtype(y), _p(row_map),
+        d_y = _empty((T * k, d), d_out.dtype, d_out)
+    if want_dgate and d_topk_w is None:
+        d_topk_w = _empty((T, k), torch.float32, d_out)
+    check(_lib.load().moe_unpermute_combine_bwd(_p(d_out), _p(y), _dtype(d_out), _p(row_map),
                                                 _p(topk_w), T, k, d, _p(d_y), _p(d_topk_w),
                                                 _stream()),
           "moe_unpermute_combine_bwd")

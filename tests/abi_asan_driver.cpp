@@ -152,6 +152,8 @@ int main(int argc, char** argv) {
   EXPECT(moe_unpermute_combine(P, MOE_BF16, PI, PF, 4, 2, 60, P, nullptr) == MOE_ERR_INVALID_ARG);
   EXPECT(moe_unpermute_combine_bwd(P, P, MOE_BF16, nullptr, PF, 4, 2, 64, P, PF, nullptr) ==
          MOE_ERR_INVALID_ARG);
+  EXPECT(moe_unpermute_combine_bwd(P, nullptr, MOE_BF16, PI, nullptr, 4, 2, 64, P, PF, nullptr) ==
+         MOE_ERR_INVALID_ARG);                          // a gate gradient needs y
   moe_mx_t mx{static_cast<uint8_t*>(P), static_cast<uint8_t*>(P), 60};
   EXPECT(moe_unpermute_combine_mx(&mx, MOE_E4M3, PI, PF, 4, 2, 64, P, MOE_BF16, nullptr) ==
          MOE_ERR_INVALID_ARG);
@@ -202,6 +204,22 @@ int main(int argc, char** argv) {
   moe_glu_bwd_args_t gb2 = gb;
   gb2.act = 7;
   EXPECT(call_cut(moe_grouped_gemm_glu_bwd, gb2, sizeof gb2) == MOE_ERR_INVALID_ARG);
+  // feature-scaling gradient without (or with too small) a workspace: refused
+  // before anything is enqueued
+  moe_glu_bwd_args_t gb3 = gb;
+  gb3.R = 8; gb3.row_scale = PF; gb3.d_row_scale = PF;
+  EXPECT(call_cut(moe_grouped_gemm_glu_bwd, gb3, sizeof gb3) == MOE_ERR_WORKSPACE);
+  gb3.ws = P; gb3.ws_bytes = moe_glu_bwd_workspace_size(8, 64) - 4;
+  EXPECT(call_cut(moe_grouped_gemm_glu_bwd, gb3, sizeof gb3) == MOE_ERR_WORKSPACE);
+  EXPECT(moe_glu_bwd_workspace_size(8, 64) == 2 * 8 * sizeof(float));
+  EXPECT(moe_glu_bwd_workspace_size(0, 64) == 0);
+
+  // ---- gates to and from row order
+  EXPECT(moe_permute_rows(PF, PI, -1, 0, PF + 64, nullptr) == MOE_ERR_INVALID_ARG);
+  EXPECT(moe_permute_rows(PF, PI, 8, 2, PF + 64, nullptr) == MOE_ERR_INVALID_ARG);
+  EXPECT(moe_permute_rows(PF, PI, 8, 0, PF, nullptr) == MOE_ERR_INVALID_ARG);   // in place
+  EXPECT(moe_permute_rows(nullptr, PI, 8, 1, PF, nullptr) == MOE_ERR_INVALID_ARG);
+  EXPECT(moe_permute_rows(nullptr, nullptr, 0, 0, nullptr, nullptr) == MOE_OK);
 
   if (g_fail == 0) std::printf("abi host checks passed\n");
   return g_fail == 0 ? 0 : 1;

@@ -57,11 +57,11 @@ class GuardedAlloc:
         assert not bad, f"writes outside a buffer: {bad}"
 
 
-def _layer(cfg, gemm, router, mx_dxp, alloc):
+def _layer(cfg, gemm, router, mx_dxp, gia, alloc):
     from ragged_grouped_gemm_amd.layer import MoEFFN
     return MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, act=cfg.act, score=cfg.score,
                   normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
-                  gemm=gemm, router=router, mx_dxp=mx_dxp, alloc=alloc)
+                  gemm=gemm, router=router, mx_dxp=mx_dxp, gate_in_act=gia, alloc=alloc)
 
 
 def _step(L, cfg, inp, gemm, router, weights):
@@ -102,31 +102,30 @@ def _buffers(L):
     return out
 
 
+_DSV3 = synth.workload("dsv3_fwdbwd", T=300, d=256, f=256, E=8, k=4, forced_empty=1)
 CASES = [
-    # (workload, gemm, router, mx_dxp)
-    (synth.workload("gptoss_fwdbwd", T=333, d=256, f=160, E=8, k=4), "bf16", False, False),
-    (synth.workload("dsv3_fwdbwd", T=300, d=256, f=256, E=8, k=4, forced_empty=1), "bf16", True,
-     False),
-    (synth.workload("dsv3_fwdbwd", T=300, d=256, f=256, E=8, k=4, forced_empty=1), "mxfp8", False,
-     True),
-    (synth.workload("dsv3_fwdbwd", T=300, d=256, f=256, E=8, k=4, forced_empty=1), "mxfp4", False,
-     False),
+    # (workload, gemm, router, mx_dxp, gates in the activation)
+    (synth.workload("gptoss_fwdbwd", T=333, d=256, f=160, E=8, k=4), "bf16", False, False, False),
+    (_DSV3, "bf16", True, False, False),
+    (_DSV3, "bf16", False, False, True),
+    (_DSV3, "mxfp8", False, True, False),
+    (_DSV3, "mxfp4", False, False, True),
 ]
 
 
-@pytest.mark.parametrize("cfg,gemm,router,mx_dxp", CASES,
-                         ids=["gptoss_bf16_bias", "dsv3_bf16_router", "dsv3_mxfp8_dxp",
-                              "dsv3_mxfp4"])
-def test_guards_and_poisoned_buffers(cfg, gemm, router, mx_dxp):
-    note(f"canary {cfg.name} {gemm} router={router} mx_dxp={mx_dxp}")
+@pytest.mark.parametrize("cfg,gemm,router,mx_dxp,gia", CASES,
+                         ids=["gptoss_bf16_bias", "dsv3_bf16_router", "dsv3_bf16_gate_in_act",
+                              "dsv3_mxfp8_dxp", "dsv3_mxfp4_gate_in_act"])
+def test_guards_and_poisoned_buffers(cfg, gemm, router, mx_dxp, gia):
+    note(f"canary {cfg.name} {gemm} router={router} mx_dxp={mx_dxp} gate_in_act={gia}")
     inp1 = synth.make_inputs(cfg)
     inp2 = synth.make_inputs(cfg.replace(seed=cfg.seed + 101))
     w = _weights(cfg, inp1, gemm, router)
     ga = GuardedAlloc()
-    L = _layer(cfg, gemm, router, mx_dxp, ga)
+    L = _layer(cfg, gemm, router, mx_dxp, gia, ga)
     _step(L, cfg, inp1, gemm, router, w)
     _step(L, cfg, inp2, gemm, router, w)
-    R = _layer(cfg, gemm, router, mx_dxp, None)
+    R = _layer(cfg, gemm, router, mx_dxp, gia, None)
     _step(R, cfg, inp2, gemm, router, w)
     torch.cuda.synchronize()
     ga.check_guards()
@@ -138,7 +137,7 @@ def test_guards_and_poisoned_buffers(cfg, gemm, router, mx_dxp):
     e2m1 = gemm == "mxfp4"
     checked = []
     for name in sorted(got):
-        if name == "ws":                 # the permute's scratch: no defined contents
+        if name in ("ws", "ds_ws"):     # scratch: no defined contents
             continue
         a, b = got[name], ref[name]
         if name.endswith("_col.data") or name.endswith("_col.scale"):

@@ -219,9 +219,17 @@ def _unpack_cols(f):
     return pos[:f], pos[f:]
 
 
+def _row_scales(rng, R):
+    """Feature-scaling factors (a zero among them), float64 and on the GPU."""
+    s = rng.uniform(0.05, 1.0, R).astype(np.float32)
+    s[::7] = 0.0
+    return s.astype(np.float64), synth.to_torch(s, "cuda")
+
+
+@pytest.mark.parametrize("scaled", [False, True], ids=["plain", "row_scale"])
 @pytest.mark.parametrize("counts,d,f", [(COUNTS_SMALL, 256, 256), (COUNTS_BIG, 1024, 512)])
-def test_mx_glu_fwd(counts, d, f):
-    note(f"mx glu fwd counts={counts} d={d} f={f}")
+def test_mx_glu_fwd(counts, d, f, scaled):
+    note(f"mx glu fwd counts={counts} d={d} f={f} scaled={scaled}")
     ops = ops_()
     rng = np.random.default_rng(11)
     E, R, n1 = len(counts), sum(counts), 2 * f
@@ -229,15 +237,18 @@ def test_mx_glu_fwd(counts, d, f):
     pad = pad_of(counts)
     _, xd = rand_bf16(rng, (R, d))
     _, wd = rand_bf16(rng, (E, n1, d), d ** -0.5)
+    sh, sd = _row_scales(rng, R) if scaled else (None, None)
     xq, wq = ops.moe_mx_quantize(xd), ops.moe_mx_quantize(wd.reshape(E * n1, d))
     (a_row, a_col), H = ops.moe_grouped_gemm_glu_fwd(xq, wq, dev(off), E=E, f=f,
-                                                    pad_offsets=dev(pad))
+                                                    pad_offsets=dev(pad), row_scale=sd)
     torch.cuda.synchronize()
     X, W = deq(xq), deq(wq).reshape(E, n1, d)
     Href = np.concatenate([X[off[e]:off[e + 1]] @ W[e].T for e in range(E)])
     assert bf16_excess(host(H), Href) <= 5e-3
     gpos, lpos = _unpack_cols(f)
     A = om.glu_forward(Href[:, gpos], Href[:, lpos], "swiglu")
+    if scaled:
+        A = om.row_scale_forward(A, sh)
     oc, os_ = omx.mx_quantize_blocks(A)
     _mx_close(u8(a_row.data), u8(a_row.scale), oc, os_, A, "A row copy")
     cc, cs = omx.mx_quantize_segments_colwise(A, off, pad)
@@ -265,10 +276,11 @@ def test_mx_gemm_fwd(counts, N, K):
     assert bf16_excess(host(y), ref) <= 5e-3
 
 
+@pytest.mark.parametrize("scaled", [False, True], ids=["plain", "row_scale"])
 @pytest.mark.parametrize("counts,d,f", [(COUNTS_SMALL, 256, 256), (COUNTS_BIG, 1024, 512),
                                         (COUNTS_BIG, 256, 1024)])
-def test_mx_glu_bwd(counts, d, f):
-    note(f"mx glu bwd counts={counts} d={d} f={f}")
+def test_mx_glu_bwd(counts, d, f, scaled):
+    note(f"mx glu bwd counts={counts} d={d} f={f} scaled={scaled}")
     ops = ops_()
     rng = np.random.default_rng(13)
     E, R, n1 = len(counts), sum(counts), 2 * f
@@ -277,13 +289,23 @@ def test_mx_glu_bwd(counts, d, f):
     _, dyd = rand_bf16(rng, (R, d))
     _, w2d = rand_bf16(rng, (E, d, f), d ** -0.5)
     h64, hd = rand_bf16(rng, (R, n1))
+    sh, sd = _row_scales(rng, R) if scaled else (None, None)
+    ds = torch.empty((R,), dtype=torch.float32, device="cuda") if scaled else None
     dyq, w2t = ops.moe_mx_quantize(dyd), ops.moe_mx_quantize_transpose(w2d)
     dh_row, dh_col = ops.moe_grouped_gemm_glu_bwd(dyq, w2t, hd, dev(off), E=E,
-                                                  pad_offsets=dev(pad))
+                                                  pad_offsets=dev(pad), row_scale=sd,
+                                                  d_row_scale=ds)
     torch.cuda.synchronize()
     DY, W2T = deq(dyq), deq(w2t).reshape(E, f, d)
     dA = np.concatenate([DY[off[e]:off[e + 1]] @ W2T[e].T for e in range(E)])
     gpos, lpos = _unpack_cols(f)
+    if scaled:
+        dA, ds_ref = om.row_scale_backward(
+            dA, om.glu_forward(h64[:, gpos], h64[:, lpos], "swiglu"), sh)
+        # dA from the scaled fp8 / fp4 MFMA, whose accumulation is coarser than
+        # float32 (as for the MX weight gradients: max |err| / rms <= 1e-3)
+        assert rel_l2(host(ds), ds_ref) <= 1e-4 and norm_err(host(ds), ds_ref) <= 1e-3, \
+            (rel_l2(host(ds), ds_ref), norm_err(host(ds), ds_ref))
     dg, dl = om.glu_backward(dA, h64[:, gpos], h64[:, lpos], "swiglu")
     dH = np.empty((R, n1))
     dH[:, gpos], dH[:, lpos] = dg, dl
@@ -362,9 +384,10 @@ LAYER_CASES = [
 ]
 
 
+@pytest.mark.parametrize("gate_in_act", [False, True], ids=["gates_in_combine", "gate_in_act"])
 @pytest.mark.parametrize("case", LAYER_CASES, ids=lambda c: f"T{c['T']}d{c['d']}f{c['f']}E{c['E']}")
-def test_mx_layer_vs_oracle(case):
-    note(f"mx layer {case}")
+def test_mx_layer_vs_oracle(case, gate_in_act):
+    note(f"mx layer {case} gate_in_act={gate_in_act}")
     from ragged_grouped_gemm_amd.layer import MoEFFN
     ops = ops_()
     cfg = synth.MoEConfig("mx_layer", gemm="mxfp8", score="sigmoid", backward=True, **case)
@@ -372,14 +395,16 @@ def test_mx_layer_vs_oracle(case):
     t = lambda a: synth.to_torch(a, "cuda")
     x, lg, W1, W2, dout = t(inp["x"]), t(inp["logits"]), t(inp["W1"]), t(inp["W2"]), t(inp["dOut"])
     W1p, _ = ops.moe_repack_glu_weights(W1)
-    L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, score="sigmoid", gemm="mxfp8")
+    L = MoEFFN(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, score="sigmoid", gemm="mxfp8",
+               gate_in_act=gate_in_act)
     Wmx = MoEFFN.mx_weights(W1p, W2)
     L.forward(x, lg, Wmx, None)
     L.backward(dout, lg, Wmx, None)
     torch.cuda.synchronize()
 
     f64 = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a
-    spec = om.LayerSpec(cfg.k, "sigmoid", True, "swiglu", store="bf16", gemm="mxfp8")
+    spec = om.LayerSpec(cfg.k, "sigmoid", True, "swiglu", store="bf16", gemm="mxfp8",
+                        gate_in_act=gate_in_act)
     fwd = om.layer_forward(f64(inp["x"]), inp["logits"], f64(inp["W1"]), f64(inp["W2"]), spec=spec)
     bwd = om.layer_backward(fwd, f64(inp["dOut"]), inp["logits"], f64(inp["W1"]), f64(inp["W2"]),
                             spec=spec)
