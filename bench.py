@@ -52,10 +52,12 @@ def parse():
                          "backward runs FC1 + GLU again (its FLOP are not counted in the metric)")
     ap.add_argument("--no-transpose-w2", action="store_true",
                     help="bf16 / fp32 training workloads: FC2's dgrad reads W2 as stored "
-                         "(MN-contiguous) instead of a transposed copy made in each backward")
+                         "(MN-contiguous) instead of a transposed copy made in each backward "
+                         "(default: the layer's choice by routed rows per expert)")
     ap.add_argument("--no-transpose-w1", action="store_true",
                     help="bf16 / fp32 training workloads: FC1's dgrad reads W1p as stored "
-                         "(MN-contiguous) instead of a transposed copy made in each backward")
+                         "(MN-contiguous) instead of a transposed copy made in each backward "
+                         "(default: the layer's choice by routed rows per expert)")
     ap.add_argument("--router", action="store_true",
                     help="the layer computes its own logits: the router's map x w_router^T fused "
                          "with the top-k routing (w_router synthetic N(0, 1/d), so the routing is "
@@ -218,7 +220,8 @@ def main():
                normalize=cfg.normalize, clamp=cfg.clamp, alpha=cfg.alpha, bias=cfg.bias,
                backward=cfg.backward, gemm=cfg.gemm, fuse_permute=args.permute == "fused",
                recompute=args.recompute, mx_dxp=args.mx_dxp,
-               transpose_w2=not args.no_transpose_w2, transpose_w1=not args.no_transpose_w1,
+               transpose_w2=False if args.no_transpose_w2 else None,
+               transpose_w1=False if args.no_transpose_w1 else None,
                router=args.router, gate_in_act=args.gate_in_act)
     if args.router:
         lg = t(synth.draw_router_weights(cfg))       # the layer's logits come from x lg^T
@@ -299,8 +302,8 @@ def main():
                    "gate_in_act": bool(args.gate_in_act),
                    "mx_dxp": bool(args.mx_dxp),
                    "dgrad_weights_transposed": [n for n, on in
-                                                (("W2", not args.no_transpose_w2 and not mx),
-                                                 ("W1p", not args.no_transpose_w1 and not mx))
+                                                (("W2", getattr(L, "W2t", None) is not None),
+                                                 ("W1p", getattr(L, "W1pt", None) is not None))
                                                 if on],
                    "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
         "pct_of_peak": round(100.0 * value / peak, 2),

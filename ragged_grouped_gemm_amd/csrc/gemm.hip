@@ -1741,6 +1741,14 @@ inline int tile_variant() {
 #endif
 }
 
+#ifdef MOE_GEMM_TUNING
+// Weight-gradient ring shapes for tuning sweeps (MOE_GEMM_WGRAD=<n>).
+inline int wgrad_variant() {
+  const char* v = getenv("MOE_GEMM_WGRAD");
+  return v ? atoi(v) : 0;
+}
+#endif
+
 template <class EL, bool AKM, bool BKM, int GROUP, int EPI, bool GATHER = false,
           bool RS = false>
 moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_t s) {
@@ -1759,6 +1767,20 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
         default: break;
       }
     }
+#ifdef MOE_GEMM_TUNING
+    if constexpr (GROUP == RAGGED_K && !AKM && !BKM && EPI == EPI_STORE && !RS) {
+      if (big) switch (wgrad_variant()) {
+          case 1:  // 48-k steps, three-deep ring (144 KB)
+            return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 2, 4, 96, 3, 2>, GATHER>(
+                p, max_cus, s);
+          case 2:  // 32-k steps, four-deep ring (128 KB)
+            return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 2, 4, 64, 4, 2>, GATHER>(
+                p, max_cus, s);
+          default:
+            break;
+        }
+    }
+#endif
     if (!big) return launch_gemm<EL, AKM, BKM, GROUP, EPI, TSmall, GATHER, RS>(p, max_cus, s);
     if constexpr (epi_glu_fwd(EPI) || epi_glu_bwd(EPI))
       return launch_gemm<EL, AKM, BKM, GROUP, EPI, TBigGlu, GATHER, RS>(p, max_cus, s);

@@ -19,11 +19,16 @@ gathering loaders address x with 31-bit byte offsets from one base, so a
 layer whose x spans 2 GiB or more (e.g. 150K tokens at d = 7168 in bf16)
 materializes Xp whatever ``fuse_permute`` says (``gather_fits``).
 
-Transposed weights for the dgrads (``transpose_w2``, ``transpose_w1``, both
-on by default): at the start of each backward W2 and W1p are copied
-transposed (``moe_transpose_weights``), so FC2's dgrad + dGLU and FC1's dgrad
-read both operands contiguous along the reduction; the results are
-bit-identical to reading the weights as stored.
+Transposed weights for the dgrads (``transpose_w2``, ``transpose_w1``): at
+the start of each backward W2 and W1p are copied transposed
+(``moe_transpose_weights``), so FC2's dgrad + dGLU and FC1's dgrad read both
+operands contiguous along the reduction; the results are bit-identical to
+reading the weights as stored.  The copies cost time in proportion to E d f,
+the dgrads gain in proportion to R d f, so by default (``None``) they are
+made when the layer averages at least ``TRANSPOSE_MIN_ROWS`` routed rows per
+expert: measured at 4096 rows per expert (16384 tokens, top-8 of 32) both
+pay (step -1.5 ms), at 1024 (8192 tokens, top-4 of 32) neither does (step
+7.30 ms with both, 7.06 ms without).
 
 Activation recomputation (``recompute=True``): the forward does not write
 the pre-activation H; the backward first runs FC1 + GLU again (from x or Xp,
@@ -90,6 +95,8 @@ class MXWeights:
 
 class MoEFFN:
     # largest x (bytes) the gather-fused loaders can address from one base
+    TRANSPOSE_MIN_ROWS = 2048   # routed rows per expert from which the dgrads' weight copies pay
+
     GATHER_MAX_BYTES = 0x7FFFFFF0
 
     @staticmethod
@@ -100,7 +107,7 @@ class MoEFFN:
     def __init__(self, T, d, f, E, k, *, dtype=torch.bfloat16, act="swiglu", score="softmax",
                  normalize=True, clamp=0.0, alpha=1.0, gelu_tanh=False, bias=False,
                  backward=True, device="cuda", max_cus=0, gemm="bf16", fuse_permute=True,
-                 recompute=False, mx_dxp=False, transpose_w2=True, transpose_w1=True,
+                 recompute=False, mx_dxp=False, transpose_w2=None, transpose_w1=None,
                  router=False, alloc=None, gate_in_act=False):
         self.T, self.d, self.f, self.E, self.k = T, d, f, E, k
         if gemm not in ("bf16", "f32", "mxfp8", "mxfp4"):
@@ -178,6 +185,9 @@ class MoEFFN:
             self.db1p = z((E, n1), f32) if bias else None
             self.db2 = z((E, d), f32) if bias else None
             # transposed weight copies for the dgrad GEMMs, refreshed every backward
+            auto = R >= self.TRANSPOSE_MIN_ROWS * E
+            transpose_w2 = auto if transpose_w2 is None else transpose_w2
+            transpose_w1 = auto if transpose_w1 is None else transpose_w1
             self.W2t = z((E, f, d), dtype) if transpose_w2 else None
             self.W1pt = z((E, d, n1), dtype) if transpose_w1 else None
 

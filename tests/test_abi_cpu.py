@@ -226,3 +226,18 @@ def test_layer_materializes_xp_when_x_is_too_large_to_gather():
     # a float32 x reaches the limit at half the tokens
     assert MoEFFN.gather_fits(80_000, 7168, torch.bfloat16)
     assert not MoEFFN.gather_fits(80_000, 7168, torch.float32)
+
+
+def test_layer_makes_transposed_weight_copies_where_they_pay():
+    """By default the dgrads' transposed weight copies are made from 2048
+    routed rows per expert on (built on the meta device: nothing runs)."""
+    from ragged_grouped_gemm_amd.layer import MoEFFN
+    dsv3 = MoEFFN(16384, 7168, 2048, 32, 8, device="meta")            # 4096 rows / expert
+    assert dsv3.W2t is not None and dsv3.W1pt is not None
+    gptoss = MoEFFN(8192, 2880, 2880, 32, 4, device="meta", bias=True)  # 1024 rows / expert
+    assert gptoss.W2t is None and gptoss.W1pt is None
+    forced = MoEFFN(8192, 2880, 2880, 32, 4, device="meta", transpose_w2=True,
+                    transpose_w1=False)
+    assert forced.W2t is not None and forced.W1pt is None
+    edge = MoEFFN(2048 * 32 // 8, 256, 256, 32, 8, device="meta")     # exactly 2048 rows / expert
+    assert edge.W2t is not None
