@@ -71,15 +71,11 @@ __global__ void __launch_bounds__(256)
     const float inv = mx_inv_scale(e);
     const long long ldb = ld / 32 * F::BYTES;
     if constexpr (F::WORDS == 8) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) word |= e4m3_code(v[q] * inv) << (8 * q);
-      *reinterpret_cast<uint32_t*>(codes + r * ldb + 32 * b + 4 * sub) = word;
+      *reinterpret_cast<uint32_t*>(codes + r * ldb + 32 * b + 4 * sub) =
+          e4m3_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     } else {
-      uint32_t half = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) half |= e2m1_code(v[q] * inv) << (4 * q);
-      *reinterpret_cast<uint16_t*>(codes + r * ldb + 16 * b + 2 * sub) = (uint16_t)half;
+      *reinterpret_cast<uint16_t*>(codes + r * ldb + 16 * b + 2 * sub) =
+          (uint16_t)e2m1_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     }
     if (sub == 0) scales[r * (ld / 32) + b] = (uint8_t)(e + 127);
   }
