@@ -104,6 +104,55 @@ def test_quantize_rows_bitexact(dtype, rows, n):
     np.testing.assert_array_equal(u8(out.scale), s)
 
 
+def _tie_blocks(fmt):
+    """float32 blocks of 32 whose largest magnitude puts the block scale at
+    2^0 (E4M3: 448 leads; E2M1: 6 leads), the other 31 values walking every
+    rounding tie of the element format (normal and subnormal) and the float32
+    neighbours on both sides, the saturation range and signed zeros; each
+    pattern block also appears scaled by 2^k for k in -24 .. 24 (same codes,
+    other scale).  NaN is not included: a block holding one has no agreed
+    scale (the oracle's maximum is NaN, the device's ignores it)."""
+    f32 = np.float32
+    vals = []
+    if fmt == "e4m3":
+        for E in range(-6, 9):                       # normal binades
+            for m in range(8):
+                t = (1.0 + (2 * m + 1) / 16.0) * 2.0 ** E  # tie between m and m + 1
+                if t < 448.0:
+                    vals.append(t)
+        for j in range(8):                           # subnormal ties: quantum 2^-9
+            vals.append((2 * j + 1) * 2.0 ** -10)
+        vals += [448.0, 449.0, 463.999, 464.0, 470.0, 500.0, 511.99]
+        lead = 448.0
+    else:
+        vals += [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 6.5, 7.0, 7.99]
+        lead = 6.0
+    vals = np.asarray(vals, dtype=f32)
+    nb = np.concatenate([np.nextafter(vals, f32(0)), vals, np.nextafter(vals, f32(np.inf))])
+    nb = np.concatenate([nb, -nb, np.array([0.0, -0.0], dtype=f32)])
+    pad = (-len(nb)) % 31
+    nb = np.concatenate([nb, np.zeros(pad, dtype=f32)]).reshape(-1, 31)
+    blocks = np.concatenate([np.full((len(nb), 1), lead, dtype=f32), nb], axis=1)
+    scaled = [blocks * f32(2.0 ** k) for k in range(-24, 25, 4)]
+    return np.concatenate(scaled).reshape(1, -1).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_quantize_rounding_ties_bitexact(fmt):
+    note(f"mx quantize ties {fmt}")
+    x = _tie_blocks(fmt)
+    n = x.shape[1] // 128 * 128
+    x = x[:, :n]
+    out = ops_().moe_mx_quantize(synth.to_torch(x, "cuda"), fmt=fmt)
+    torch.cuda.synchronize()
+    c, s = omx.mx_quantize_blocks(x.astype(np.float64), fmt=fmt)
+    got = u8(out.data)
+    if fmt == "e2m1":
+        got = omx.unpack_fp4(got)
+    np.testing.assert_array_equal(got, c)
+    np.testing.assert_array_equal(u8(out.scale), s)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quantize_transpose_bitexact(dtype):
     note(f"mx quantize transpose {dtype}")
