@@ -1230,8 +1230,10 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       // have read step j by the end of phase 2 j + 1, so step j + S is loaded
       // into step j's slot at the start of phase 2 j + 2; the loads of step
       // j + 1 are waited for at the end of phase 2 j + 1.
-      static_assert(C::WGM == 2 && !MX, "ping-pong needs two wave groups");
-      const int grp = wm;
+      // (with 4 wave rows, rows 0 and 2 form group 0 and rows 1 and 3 group 1:
+      // each SIMD then holds two waves of each group)
+      static_assert(C::WGM % 2 == 0 && !MX, "ping-pong needs two wave groups");
+      const int grp = wm & 1;
 #pragma unroll
       for (int st = S_ - 1; st < S_; ++st)
         if (st < nk) {
@@ -1776,6 +1778,13 @@ moe_status_t dispatch_tiles(const GemmArgs& p, bool big, int max_cus, hipStream_
           case 2:  // 32-k steps, four-deep ring (128 KB)
             return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 2, 4, 64, 4, 2>, GATHER>(
                 p, max_cus, s);
+          case 3:  // 16 waves (64 x 64 each) in two ping-pong groups, 32-k steps, 4-deep
+            return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 4, 4, 64, 4, 2>, GATHER>(
+                p, max_cus, s);
+          case 4:  // the same with a two-deep ring
+            return launch_gemm<EL, AKM, BKM, GROUP, EPI, Tile<256, 256, 4, 4, 64, 2, 2>, GATHER>(
+                p, max_cus, s);
+
           default:
             break;
         }
