@@ -123,6 +123,7 @@ struct GemmArgs {
   int accumulate;
   int gm;  // M-tiles per band of the tile order
   int snake;  // RAGGED_K: odd rounds of the tile order run backwards
+  int glu_direct;  // tuning builds only: FC1 + GLU stores without the LDS staging (1), or A's (2)
   // Gather-fused permute (nullable): RAGGED_M reads row r of A as row
   // gather[r] of a; RAGGED_K reads k-row r of B as row gather[r] of b; the
   // gathered source has gather_rows rows.
@@ -1430,6 +1431,15 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     // already reach 1.03-1.08x)
     constexpr bool kStaged = EPI == EPI_STORE && GROUP == RAGGED_M && !MX && AKM && BKM &&
                              TL::SCHED != 2 && C::template stage_fits<OT>();
+    // FC1 + GLU (bf16, 64-column wave tiles): H and A through LDS the same way
+    constexpr bool kStagedGlu = epi_glu_fwd(EPI) && GROUP == RAGGED_M && !MX &&
+                                TL::SCHED != 2 && sizeof(SO) == 2 && C::WTN == 64 &&
+                                (THREADS / 64) * 32 * (C::WTN * 2 + C::WTN) <= C::STAGE_U4 * 16;
+#ifdef MOE_GEMM_TUNING
+    const bool glu_direct = p.glu_direct == 1, glu_a_direct = p.glu_direct == 2;
+#else
+    constexpr bool glu_direct = false, glu_a_direct = false;
+#endif
     bool mx_store = false;  // plain product written as an MX row copy instead of C
     if constexpr (MX && EPI == EPI_STORE && GROUP == RAGGED_M) mx_store = p.mxr != nullptr;
     if (mx_store) {
@@ -1576,6 +1586,86 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
           }
         }
       });
+    } else if (kStagedGlu && !glu_direct && p.aux) {
+      if constexpr (kStagedGlu) {
+      // FC1 + GLU through LDS: for each 32-row block the wave stages its 64
+      // packed H columns (128-byte rows, chunk c of row r at c ^ ((r >> 1) &
+      // 7)) and its 32 A columns (64-byte rows, chunk c at c ^ ((r >> 1) & 3))
+      // in the ring slot that no wave reads any more (as the plain staged
+      // epilogue below), then writes whole rows, 16 bytes per lane.  Same
+      // values and rounding as epi_glu_fwd.  (Only where H is stored: A's
+      // 64-byte rows alone gain nothing over the direct stores, and the LDS
+      // round trip then costs 4 % on a forward-only Mixtral-size layer.)
+      constexpr int CH = C::WTN * 2 / 16;   // 16-byte chunks per staged H row
+      constexpr int CA = C::WTN / 16;       // per staged A row
+      u32x4* Hs = stage_ptr(nk) + wave * 32 * (CH + CA);
+      u32x4* As = Hs + 32 * CH;
+      char* Hb = reinterpret_cast<char*>(Hs);
+      char* Ab = reinterpret_cast<char*>(As);
+      auto hslot = [](int rr, int c) { return c ^ ((rr >> 1) & 7); };
+      auto aslot = [](int rr, int c) { return c ^ ((rr >> 1) & 3); };
+      const float* bias = p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr;
+      const int r = lane & 31, h = lane >> 5;
+      const int wc0 = n0 + wn * C::WTN;     // the wave's first packed column (a multiple of 64)
+      SO* Hg = reinterpret_cast<SO*>(p.aux);
+      SO* Ag = reinterpret_cast<SO*>(p.c);
+      static_for<0, TM>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int rbase = m0 + wm * C::WTM + 32 * i;
+        const int row_l = rbase + r;
+        const float sc = (RS && p.row_scale && row_l < mlim) ? p.row_scale[row_l] : 1.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cl = 8 * g + 4 * h;       // gate column in the wave (linear: + 32)
+          const int colg = wc0 + cl;
+          const bool cok = colg < p.N;
+          float gv[4], lv[4], o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gv[q] = acc[i][0][4 * g + q] + ((bias && cok) ? bias[colg + q] : 0.0f);
+            lv[q] = acc[i][1][4 * g + q] + ((bias && cok) ? bias[colg + 32 + q] : 0.0f);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float gt = gv[q], li = lv[q];
+            if (p.clamp > 0.0f) {
+              gt = fminf(gt, p.clamp);
+              li = fminf(fmaxf(li, -p.clamp), p.clamp);
+            }
+            o[q] = act_value<epi_act(EPI)>(gt, p.alpha, p.gelu_tanh) * li * sc;
+          }
+          *reinterpret_cast<u32x2*>(Hb + (r * CH + hslot(r, cl / 8)) * 16 + (cl % 8) * 2) =
+              u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+          *reinterpret_cast<u32x2*>(Hb + (r * CH + hslot(r, (cl + 32) / 8)) * 16 + (cl % 8) * 2) =
+              u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+          if (glu_a_direct) {
+            if (row_l < mlim && cok) store4(Ag + (size_t)row_l * p.ldc + wc0 / 2 + cl, o);
+          } else {
+            *reinterpret_cast<u32x2*>(Ab + (r * CA + aslot(r, cl / 8)) * 16 + (cl % 8) * 2) =
+                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < 32 * CH / 64; ++it) {
+          const int rr = it * (64 / CH) + lane / CH, cc = lane % CH;
+          const u32x4 v = Hs[rr * CH + hslot(rr, cc)];
+          const int row = rbase + rr, col = wc0 + cc * 8;
+          if (row < mlim && col < p.N)
+            *reinterpret_cast<u32x4*>(Hg + (size_t)row * p.ld_aux + col) = v;
+        }
+#pragma unroll
+        for (int it = 0; it < 32 * CA / 64; ++it) {
+          if (glu_a_direct) break;
+          const int rr = it * (64 / CA) + lane / CA, cc = lane % CA;
+          const u32x4 v = As[rr * CA + aslot(rr, cc)];
+          const int row = rbase + rr, col = wc0 / 2 + cc * 8;
+          if (row < mlim && col < p.N / 2)
+            *reinterpret_cast<u32x4*>(Ag + (size_t)row * p.ldc + col) = v;
+        }
+        wave_lds_sync();
+      });
+      }
     } else if (kStaged && !(GROUP == RAGGED_K && p.accumulate)) {
       if constexpr (kStaged) {
         // Plain epilogue through LDS: each wave stages 32 rows x WTN columns of
@@ -1857,8 +1947,10 @@ moe_status_t dispatch(int dtype, const GemmArgs& p, bool big, int max_cus, hipSt
 }
 
 // Band height 4 and the weight gradients' alternating tile order.  (A
-// -DMOE_GEMM_TUNING build lets MOE_GEMM_GM override the band height and
-// MOE_GEMM_SNAKE=0 turn the alternating order off, for tuning sweeps.)
+// -DMOE_GEMM_TUNING build lets MOE_GEMM_GM override the band height,
+// MOE_GEMM_SNAKE=0 turn the alternating order off and MOE_GEMM_GLU_DIRECT=1
+// (2) store the FC1 + GLU outputs (A) without the LDS staging, for tuning
+// sweeps.)
 inline GemmArgs zero_args() {
   GemmArgs p;
   memset(&p, 0, sizeof(p));
@@ -1871,6 +1963,7 @@ inline GemmArgs zero_args() {
     if (g >= 1 && g <= 64) p.gm = g;
   }
   if (const char* v = getenv("MOE_GEMM_SNAKE")) p.snake = atoi(v) != 0;
+  if (const char* v = getenv("MOE_GEMM_GLU_DIRECT")) p.glu_direct = atoi(v);
 #endif
   return p;
 }
