@@ -200,6 +200,40 @@ def test_glu_fwd_bf16(counts, d, f, act, clamp, alpha, gtanh, bias):
     assert bf16_excess(host(A), Ao) <= TOL_BF16 / 4
 
 
+@pytest.mark.parametrize("counts", [COUNTS_BIG, COUNTS_SMALL])
+@pytest.mark.parametrize("act,clamp,gtanh,bias,scaled", [
+    ("swiglu", 1.5, False, True, False), ("geglu", 0.0, True, False, True),
+    ("swiglu", 0.0, False, False, True)])
+def test_glu_fwd_h_saved_and_forward_only_agree(counts, act, clamp, gtanh, bias, scaled):
+    """A with H saved (whole-row stores staged through LDS) equals, bit for
+    bit, A of a forward-only call (direct stores), at f = 352: 2f = 704
+    packed columns, so the last 256-column tile holds three live wave
+    columns and one dead one; also against the oracle."""
+    d, f = 512, 352
+    note(f"glu_fwd staged vs direct R={sum(counts)} d={d} f={f} {act} scaled={scaled}")
+    rng, off, offd = _setup(counts, 3 * d + f)
+    E, R = len(counts), int(off[-1])
+    xh, xd = rand_bf16(rng, (R, d))
+    Wh, Wd = rand_bf16(rng, (E, 2 * f, d), d ** -0.5)
+    bh, bd = rand_f32(rng, (E, 2 * f)) if bias else (None, None)
+    sh = rng.uniform(0.1, 1.0, R) if scaled else None
+    sd = torch.tensor(sh, dtype=torch.float32, device="cuda") if scaled else None
+    Wpd, bpd = ops.moe_repack_glu_weights(Wd, bd)
+    A1, H = ops.moe_grouped_gemm_glu_fwd(xd, Wpd, offd, b1p=bpd, act=act, clamp=clamp,
+                                         gelu_tanh=gtanh, row_scale=sd)
+    A0, none = ops.moe_grouped_gemm_glu_fwd(xd, Wpd, offd, b1p=bpd, act=act, clamp=clamp,
+                                            gelu_tanh=gtanh, save_h=False, row_scale=sd)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(A1.view(torch.int16), A0.view(torch.int16))
+    Hc = om.grouped_linear(xh, Wh, off, bh)
+    Ao = om.glu_forward(Hc[:, :f], Hc[:, f:], act, clamp, 1.0, gtanh)
+    if scaled:
+        Ao = om.row_scale_forward(Ao, sh.astype(np.float32).astype(np.float64))
+    assert bf16_excess(host(H), om.repack_glu(Hc[None], G=G, axis=2)[0]) <= TOL_BF16 / 4
+    assert bf16_excess(host(A1), Ao) <= TOL_BF16 / 4
+
+
 @pytest.mark.parametrize("counts,d,f", [(COUNTS_SMALL, 128, 256), (COUNTS_BIG, 256, 512)])
 @pytest.mark.parametrize("act,clamp", [("swiglu", 0.0), ("swiglu", 7.0), ("srelu", 0.0)])
 def test_glu_fwd_f32(counts, d, f, act, clamp):
