@@ -1467,10 +1467,12 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     // (built where it needs no spills: the plain bf16 epilogue of tiles with
     // both operands K-contiguous and the pinned or compiler schedule -- FC2
     // and the FC1 dgrad from the transposed weights -- whose direct stores
-    // wrote 1.58x the output bytes; the weight gradients' float32 stores
-    // already reach 1.03-1.08x)
-    constexpr bool kStaged = EPI == EPI_STORE && GROUP == RAGGED_M && !MX && AKM && BKM &&
-                             TL::SCHED != 2 && C::template stage_fits<OT>();
+    // wrote 1.58x the output bytes; and the weight gradients' float32 stores,
+    // which already wrote 1.03-1.08x but cost 9 % of those kernels as
+    // 32-byte pieces of 32 rows per store, 3 % less as whole rows)
+    constexpr bool kStaged = EPI == EPI_STORE && !MX &&
+                             (GROUP == RAGGED_K || (AKM && BKM && TL::SCHED != 2)) &&
+                             C::template stage_fits<OT>();
     // FC1 + GLU (bf16, 64-column wave tiles): H and A through LDS the same way
     constexpr bool kStagedGlu = epi_glu_fwd(EPI) && GROUP == RAGGED_M && !MX &&
                                 TL::SCHED != 2 && sizeof(SO) == 2 && C::WTN == 64 &&
@@ -1756,7 +1758,12 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         const float* bias = (GROUP == RAGGED_M && p.bias) ? p.bias + (size_t)e * p.ld_bias : nullptr;
         OT* Cg = reinterpret_cast<OT*>(p.c);
         if constexpr (GROUP == RAGGED_K) Cg += (size_t)e * p.c_expert_stride;
-        const int r = lane & 31, h = lane >> 5;
+        // the lane's staging addresses are computed here, per tile: hoisted
+        // out of the tile loop they would be held (or spilled) through the
+        // main loop
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int r = lane_e & 31, h = lane_e >> 5;
         static_for<0, TM>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
           static_for<0, TN>([&](auto jc) {
@@ -1782,7 +1789,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
           wave_lds_sync();
 #pragma unroll
           for (int it = 0; it < 32 / RPI; ++it) {
-            const int rr = it * RPI + lane / CPRW, cc = lane % CPRW;
+            const int rr = it * RPI + lane_e / CPRW, cc = lane_e % CPRW;
             const u32x4 v = Wt[rr * CPRW + slot(rr, cc)];
             const int row = m0 + wm * C::WTM + 32 * i + rr;
             const int col = n0 + wn * C::WTN + cc * EPC;
