@@ -1036,12 +1036,20 @@ struct GemmCfg {
   static constexpr int STAGE_WAVES = STAGE_U4 * 16 / (MX_STAGE_FLOATS * 4);
   static constexpr int MX_SLOTS = (THREADS / 64 + STAGE_WAVES - 1) / STAGE_WAVES;
   // The plain epilogue can stage 32 rows of each wave's tile (in the output
-  // type OT) in the free ring slot before writing whole rows, where every
-  // wave's rows fit in it.
+  // type OT) in the ring slots free after the main loop before writing whole
+  // rows, where every wave's rows fit in them.
   template <class OT>
   static constexpr bool stage_fits() {
-    return (THREADS / 64) * 32 * WTN * (int)sizeof(OT) <= STAGE_U4 * 16 &&
+    return stage_waves<OT>() >= 1 &&
+           (THREADS / 64 + stage_waves<OT>() - 1) / stage_waves<OT>() <= STAGES - 1 &&
            (WTN * (int)sizeof(OT) == 128 || WTN * (int)sizeof(OT) == 256);
+  }
+  // waves whose 32-row staging tiles fit one ring slot (the staged plain
+  // epilogue spreads the waves over the STAGES - 1 slots free after the main
+  // loop)
+  template <class OT>
+  static constexpr int stage_waves() {
+    return STAGE_U4 * 16 / (32 * WTN * (int)sizeof(OT));
   }
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(!epi_glu_fwd(EPI) || WTN % 64 == 0, "GLU pairs need 64-column wave tiles");
@@ -1470,7 +1478,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     // wrote 1.58x the output bytes; and the weight gradients' float32 stores,
     // which already wrote 1.03-1.08x but cost 9 % of those kernels as
     // 32-byte pieces of 32 rows per store, 3 % less as whole rows)
-    constexpr bool kStaged = EPI == EPI_STORE && !MX &&
+    constexpr bool kStaged = EPI == EPI_STORE && (!MX || GROUP == RAGGED_K) &&
                              (GROUP == RAGGED_K || (AKM && BKM && TL::SCHED != 2)) &&
                              C::template stage_fits<OT>();
     // FC1 + GLU (bf16, 64-column wave tiles): H and A through LDS the same way
@@ -1739,10 +1747,11 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     } else if (kStaged && !(GROUP == RAGGED_K && p.accumulate)) {
       if constexpr (kStaged) {
         // Plain epilogue through LDS: each wave stages 32 rows x WTN columns of
-        // its tile at a time in the ring slot that no wave reads any more
-        // (nk % STAGES: its last reader passed the barrier of the last step,
-        // and no load is in flight into it; the next tile's loads start after
-        // the tile barrier), then writes whole rows -- 16 bytes per lane, a
+        // its tile at a time in a ring slot that no wave reads any more
+        // (nk % STAGES onwards, up to STAGES - 1 slots: their last readers
+        // passed the barrier of the last step, and no load is in flight into
+        // them; the next tile's loads start after the tile barrier), then
+        // writes whole rows -- 16 bytes per lane, a
         // row's WTN columns contiguous -- instead of 16-byte pieces of 32 rows
         // per store.  Chunk c (16 bytes) of staged row r sits at c ^ ((r >> 1)
         // & 7) for 128-byte rows or c ^ (r & 15) for 256-byte rows, so the
@@ -1753,7 +1762,8 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         constexpr int EPC = 16 / OB;               // elements per chunk
         constexpr int RPI = 64 / CPRW;             // staged rows per wave instruction
         auto slot = [](int r, int c) { return CPRW == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15)); };
-        u32x4* Wt = stage_ptr(nk) + wave * 32 * CPRW;
+        constexpr int SW = C::template stage_waves<OT>();
+        u32x4* Wt = stage_ptr(nk + wave / SW) + (wave % SW) * 32 * CPRW;
         char* Wb = reinterpret_cast<char*>(Wt);
         const float* bias = (GROUP == RAGGED_M && p.bias) ? p.bias + (size_t)e * p.ld_bias : nullptr;
         OT* Cg = reinterpret_cast<OT*>(p.c);
