@@ -683,8 +683,33 @@ __device__ __forceinline__ void epi_glu_bwd(const S* __restrict__ Hrow, S* __res
   }
 }
 
-// The same for bf16 H already in registers: h[g] = {gate, linear} bits of the
-// four values at A columns c0 + 8 g .. + 3.
+// The same for bf16 H already in registers: hg = {gate, linear} bits of the
+// four values at A columns c0 + 8 g .. + 3; dg, dl get their gradients.
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_raw_group(const u32x2 (&hg)[2], const f32x16& acc, int g,
+                                                  float L, float alpha, int gtanh, float sc,
+                                                  float& ps, float (&dg)[4], float (&dl)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t wg = hg[0][q >> 1], wl = hg[1][q >> 1];
+    float gt = bf16_bits_to_f32((q & 1) ? (wg >> 16) : (wg & 0xffffu));
+    float li = bf16_bits_to_f32((q & 1) ? (wl >> 16) : (wl & 0xffffu));
+    float mg = 1.0f, ml = 1.0f;
+    if (L > 0.0f) {
+      mg = gt <= L ? 1.0f : 0.0f;
+      ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
+      gt = fminf(gt, L);
+      li = fminf(fmaxf(li, -L), L);
+    }
+    float a, da_dg;
+    act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
+    ps += acc[4 * g + q] * (a * li);
+    const float d = acc[4 * g + q] * sc;
+    dg[q] = d * li * da_dg * mg;
+    dl[q] = d * a * ml;
+  }
+}
+
 template <int ACT>
 __device__ __forceinline__ void epi_glu_bwd_raw(const u32x2 (&h)[4][2], uint16_t* __restrict__ Drow,
                                                 const f32x16& acc, int c0, int N, float L,
@@ -695,25 +720,7 @@ __device__ __forceinline__ void epi_glu_bwd_raw(const u32x2 (&h)[4][2], uint16_t
     if (col >= N) continue;
     const int pg = (col >> 5) * 64 + (col & 31);
     float dg[4], dl[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t wg = h[g][0][q >> 1], wl = h[g][1][q >> 1];
-      float gt = bf16_bits_to_f32((q & 1) ? (wg >> 16) : (wg & 0xffffu));
-      float li = bf16_bits_to_f32((q & 1) ? (wl >> 16) : (wl & 0xffffu));
-      float mg = 1.0f, ml = 1.0f;
-      if (L > 0.0f) {
-        mg = gt <= L ? 1.0f : 0.0f;
-        ml = (li >= -L && li <= L) ? 1.0f : 0.0f;
-        gt = fminf(gt, L);
-        li = fminf(fmaxf(li, -L), L);
-      }
-      float a, da_dg;
-      act_value_grad<ACT>(gt, alpha, gtanh, a, da_dg);
-      ps += acc[4 * g + q] * (a * li);
-      const float d = acc[4 * g + q] * sc;
-      dg[q] = d * li * da_dg * mg;
-      dl[q] = d * a * ml;
-    }
+    glu_bwd_raw_group<ACT>(h[g], acc, g, L, alpha, gtanh, sc, ps, dg, dl);
     store4(Drow + pg, dg);
     store4(Drow + pg + 32, dl);
   }
@@ -1485,6 +1492,11 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     constexpr bool kStagedGlu = epi_glu_fwd(EPI) && GROUP == RAGGED_M && !MX &&
                                 TL::SCHED != 2 && sizeof(SO) == 2 && C::WTN == 64 &&
                                 (THREADS / 64) * 32 * (C::WTN * 2 + C::WTN) <= C::STAGE_U4 * 16;
+    // FC2 dgrad + dGLU (bf16, 64-column wave tiles, no feature-scaling
+    // gradient: with it the kernel spills): dH through LDS as 256-byte rows
+    constexpr bool kStagedDglu = epi_glu_bwd(EPI) && GROUP == RAGGED_M && !MX && !RS &&
+                                 TL::SCHED != 2 && sizeof(SO) == 2 && C::WTN == 64 &&
+                                 (THREADS / 64) * 32 * (C::WTN * 2 * 2) <= C::STAGE_U4 * 16;
 #ifdef MOE_GEMM_TUNING
     const bool glu_direct = p.glu_direct == 1, glu_a_direct = p.glu_direct == 2;
 #else
@@ -1646,6 +1658,65 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         }
       };
       hload(0, hr[0]);
+      if (kStagedDglu && !glu_direct) {
+        if constexpr (kStagedDglu) {
+        // dH through LDS: for each 32-row block the wave stages its 128 packed
+        // dH columns (256-byte rows, chunk c of row r at c ^ (r & 15)) in the
+        // ring slot that no wave reads any more, then writes whole rows, 16
+        // bytes per lane.  Same values and rounding as the direct stores.
+        // (Lane-dependent addresses are computed here, per tile, behind an
+        // empty asm: hoisted out of the tile loop they would be spilled.)
+        constexpr int CD = C::WTN * 2 * 2 / 16;   // 16-byte chunks per staged dH row
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int r = lane_e & 31, h = lane_e >> 5;
+        u32x4* Ds = stage_ptr(nk) + wave * 32 * CD;
+        char* Dr = reinterpret_cast<char*>(Ds) + r * CD * 16 + 8 * h;   // the lane's staged row
+        const int wc0 = n0 + wn * C::WTN;     // the wave's first A column (a multiple of 64)
+        SO* Dg = reinterpret_cast<SO*>(p.c);
+        static_for<0, TM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const int rbase = m0 + wm * C::WTM + 32 * i;
+          const int row = rbase + r;
+          if (row < mlim) {
+            const float sc = (RS && p.row_scale) ? p.row_scale[row] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const int cb = wc0 + 32 * j;
+              float ps = 0.0f;
+              if (cb < p.N) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  float dg[4], dl[4];
+                  glu_bwd_raw_group<epi_act(EPI)>(hr[i & 1][j][g], acc[i][j], g, p.clamp,
+                                                  p.alpha, p.gelu_tanh, sc, ps, dg, dl);
+                  // packed columns 64 j + 8 g + 4 h (gate) and 32 further (linear)
+                  *reinterpret_cast<u32x2*>(Dr + ((8 * j + g) ^ (r & 15)) * 16) =
+                      u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+                  *reinterpret_cast<u32x2*>(Dr + ((8 * j + 4 + g) ^ (r & 15)) * 16) =
+                      u32x2{pack_bf16x2(dl[0], dl[1]), pack_bf16x2(dl[2], dl[3])};
+                }
+              }
+              if constexpr (RS)
+                if (p.ds_part) ds_block_store(p.ds_part, p.ld_ds, cb >> 5, row, cb < p.N, ps);
+            }
+          }
+          // the next block's H is requested once this block's is used; its
+          // latency hides behind the row stores below
+          if constexpr (i + 1 < TM) hload(i + 1, hr[(i + 1) & 1]);
+          wave_lds_sync();
+#pragma unroll
+          for (int it = 0; it < 32 * CD / 64; ++it) {
+            const int rr = it * (64 / CD) + lane_e / CD, cc = lane_e % CD;
+            const u32x4 v = Ds[rr * CD + (cc ^ (rr & 15))];
+            const int orow = rbase + rr;
+            if (orow < mlim && wc0 + 32 * (cc / 8) < p.N)
+              *reinterpret_cast<u32x4*>(Dg + (size_t)orow * p.ldc + 2 * wc0 + cc * 8) = v;
+          }
+          wave_lds_sync();
+        });
+        }
+      } else {
       static_for<0, TM>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i + 1 < TM) hload(i + 1, hr[(i + 1) & 1]);
@@ -1664,6 +1735,7 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
           }
         }
       });
+      }
     } else if (kStagedGlu && !glu_direct && p.aux) {
       if constexpr (kStagedGlu) {
       // FC1 + GLU through LDS: for each 32-row block the wave stages its 64

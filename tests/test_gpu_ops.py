@@ -234,6 +234,35 @@ def test_glu_fwd_h_saved_and_forward_only_agree(counts, act, clamp, gtanh, bias,
     assert bf16_excess(host(A1), Ao) <= TOL_BF16 / 4
 
 
+@pytest.mark.parametrize("counts", [COUNTS_BIG, COUNTS_SMALL])
+@pytest.mark.parametrize("act,clamp,gtanh", [("swiglu", 1.5, False), ("geglu", 0.0, True)])
+def test_glu_bwd_staged_equals_direct(counts, act, clamp, gtanh):
+    """dH without a feature scale (bf16: stored through LDS as whole rows)
+    equals, bit for bit, dH with a unit feature scale (the kernel variant
+    that also sums the scale's gradient, which stores dH directly), at f =
+    352: the last 256-column tile holds three live wave columns and one dead
+    one; also against the oracle."""
+    d, f = 512, 352
+    note(f"glu_bwd staged vs direct R={sum(counts)} d={d} f={f} {act} clamp={clamp}")
+    rng, off, offd = _setup(counts, 7 * d + f)
+    E, R = len(counts), int(off[-1])
+    dyh, dyd = rand_bf16(rng, (R, d))
+    w2h, w2d = rand_bf16(rng, (E, d, f), d ** -0.5)
+    hh, hd = rand_bf16(rng, (R, 2 * f))
+    dh0 = ops.moe_grouped_gemm_glu_bwd(dyd, w2d, hd, offd, act=act, clamp=clamp, gelu_tanh=gtanh)
+    ones = torch.ones(R, dtype=torch.float32, device="cuda")
+    ds = torch.empty(R, dtype=torch.float32, device="cuda")
+    dh1 = ops.moe_grouped_gemm_glu_bwd(dyd, w2d, hd, offd, act=act, clamp=clamp, gelu_tanh=gtanh,
+                                       row_scale=ones, d_row_scale=ds)
+    torch.cuda.synchronize()
+    assert torch.equal(dh0.view(torch.int16), dh1.view(torch.int16))
+    dA = om.grouped_dgrad(dyh, w2h, off)
+    hc = om.unpack_glu(hh[None], G=G, axis=2)[0]
+    dg, dl = om.glu_backward(dA, hc[:, :f], hc[:, f:], act, clamp, 1.0, gtanh)
+    ref = om.repack_glu(np.concatenate([dg, dl], 1)[None], G=G, axis=2)[0]
+    assert bf16_excess(host(dh0), ref) <= TOL_BF16 / 4
+
+
 @pytest.mark.parametrize("counts,d,f", [(COUNTS_SMALL, 128, 256), (COUNTS_BIG, 256, 512)])
 @pytest.mark.parametrize("act,clamp", [("swiglu", 0.0), ("swiglu", 7.0), ("srelu", 0.0)])
 def test_glu_fwd_f32(counts, d, f, act, clamp):
