@@ -1736,16 +1736,14 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
         }
       });
       }
-    } else if (kStagedGlu && !glu_direct && p.aux) {
+    } else if (kStagedGlu && !glu_direct) {
       if constexpr (kStagedGlu) {
       // FC1 + GLU through LDS: for each 32-row block the wave stages its 64
       // packed H columns (128-byte rows, chunk c of row r at c ^ ((r >> 1) &
       // 7)) and its 32 A columns (64-byte rows, chunk c at c ^ ((r >> 1) & 3))
       // in the ring slot that no wave reads any more (as the plain staged
-      // epilogue below), then writes whole rows, 16 bytes per lane.  Same
-      // values and rounding as epi_glu_fwd.  (Only where H is stored: A's
-      // 64-byte rows alone gain nothing over the direct stores, and the LDS
-      // round trip then costs 4 % on a forward-only Mixtral-size layer.)
+      // epilogue below), then writes whole rows, 16 bytes per lane (H only
+      // when it is saved).  Same values and rounding as epi_glu_fwd.
       constexpr int CH = C::WTN * 2 / 16;   // 16-byte chunks per staged H row
       constexpr int CA = C::WTN / 16;       // per staged A row
       u32x4* Hs = stage_ptr(nk) + wave * 32 * (CH + CA);
@@ -1755,7 +1753,12 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
       auto hslot = [](int rr, int c) { return c ^ ((rr >> 1) & 7); };
       auto aslot = [](int rr, int c) { return c ^ ((rr >> 1) & 3); };
       const float* bias = p.bias ? p.bias + (size_t)e * p.ld_bias : nullptr;
-      const int r = lane & 31, h = lane >> 5;
+      // lane-dependent addresses are computed here, per tile, behind an
+      // empty asm: hoisted out of the tile loop they would be held (or
+      // spilled) through the main loop
+      int lane_e = lane;
+      asm volatile("" : "+v"(lane_e));
+      const int r = lane_e & 31, h = lane_e >> 5;
       const int wc0 = n0 + wn * C::WTN;     // the wave's first packed column (a multiple of 64)
       SO* Hg = reinterpret_cast<SO*>(p.aux);
       SO* Ag = reinterpret_cast<SO*>(p.c);
@@ -1784,10 +1787,12 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
             }
             o[q] = act_value<epi_act(EPI)>(gt, p.alpha, p.gelu_tanh) * li * sc;
           }
-          *reinterpret_cast<u32x2*>(Hb + (r * CH + hslot(r, cl / 8)) * 16 + (cl % 8) * 2) =
-              u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
-          *reinterpret_cast<u32x2*>(Hb + (r * CH + hslot(r, (cl + 32) / 8)) * 16 + (cl % 8) * 2) =
-              u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+          if (Hg) {
+            *reinterpret_cast<u32x2*>(Hb + (r * CH + hslot(r, cl / 8)) * 16 + (cl % 8) * 2) =
+                u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+            *reinterpret_cast<u32x2*>(Hb + (r * CH + hslot(r, (cl + 32) / 8)) * 16 + (cl % 8) * 2) =
+                u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+          }
           if (glu_a_direct) {
             if (row_l < mlim && cok) store4(Ag + (size_t)row_l * p.ldc + wc0 / 2 + cl, o);
           } else {
@@ -1796,18 +1801,20 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
           }
         }
         wave_lds_sync();
+        if (Hg) {
 #pragma unroll
-        for (int it = 0; it < 32 * CH / 64; ++it) {
-          const int rr = it * (64 / CH) + lane / CH, cc = lane % CH;
-          const u32x4 v = Hs[rr * CH + hslot(rr, cc)];
-          const int row = rbase + rr, col = wc0 + cc * 8;
-          if (row < mlim && col < p.N)
-            *reinterpret_cast<u32x4*>(Hg + (size_t)row * p.ld_aux + col) = v;
+          for (int it = 0; it < 32 * CH / 64; ++it) {
+            const int rr = it * (64 / CH) + lane_e / CH, cc = lane_e % CH;
+            const u32x4 v = Hs[rr * CH + hslot(rr, cc)];
+            const int row = rbase + rr, col = wc0 + cc * 8;
+            if (row < mlim && col < p.N)
+              *reinterpret_cast<u32x4*>(Hg + (size_t)row * p.ld_aux + col) = v;
+          }
         }
 #pragma unroll
         for (int it = 0; it < 32 * CA / 64; ++it) {
           if (glu_a_direct) break;
-          const int rr = it * (64 / CA) + lane / CA, cc = lane % CA;
+          const int rr = it * (64 / CA) + lane_e / CA, cc = lane_e % CA;
           const u32x4 v = As[rr * CA + aslot(rr, cc)];
           const int row = rbase + rr, col = wc0 / 2 + cc * 8;
           if (row < mlim && col < p.N / 2)

@@ -205,10 +205,10 @@ def test_glu_fwd_bf16(counts, d, f, act, clamp, alpha, gtanh, bias):
     ("swiglu", 1.5, False, True, False), ("geglu", 0.0, True, False, True),
     ("swiglu", 0.0, False, False, True)])
 def test_glu_fwd_h_saved_and_forward_only_agree(counts, act, clamp, gtanh, bias, scaled):
-    """A with H saved (whole-row stores staged through LDS) equals, bit for
-    bit, A of a forward-only call (direct stores), at f = 352: 2f = 704
-    packed columns, so the last 256-column tile holds three live wave
-    columns and one dead one; also against the oracle."""
+    """A with H saved equals, bit for bit, A of a forward-only call (which
+    stages and writes A alone), at f = 352: 2f = 704 packed columns, so the
+    last 256-column tile holds three live wave columns and one dead one;
+    also against the oracle."""
     d, f = 512, 352
     note(f"glu_fwd staged vs direct R={sum(counts)} d={d} f={f} {act} scaled={scaled}")
     rng, off, offd = _setup(counts, 3 * d + f)
