@@ -1506,23 +1506,37 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
     if constexpr (MX && EPI == EPI_STORE && GROUP == RAGGED_M) mx_store = p.mxr != nullptr;
     if (mx_store) {
       if constexpr (MX && EPI == EPI_STORE && GROUP == RAGGED_M) {
-        // each 32 x 32 block passes through the wave's staging tile; lanes
-        // 0-31 quantize one row of it each (blocks of 32 columns)
+        // the 32 x 32 blocks of column blocks j and j + 1 pass through two
+        // staging tiles of the wave together; lanes 0-31 quantize one row
+        // each of the first, lanes 32-63 of the second (blocks of 32
+        // columns).  The second tiles may reach into the last step's ring
+        // slot, which all waves have finished reading past this barrier.
+        constexpr int NW = THREADS / 64;
+        static_assert(2 * NW <= C::STAGES * C::STAGE_WAVES && TN % 2 == 0,
+                      "two staging areas per wave");
+        __syncthreads();
         float* Wt = reinterpret_cast<float*>(stage_ptr(nk + wave / C::STAGE_WAVES)) +
                     (wave % C::STAGE_WAVES) * C::MX_STAGE_FLOATS;
+        float* Wt2 = reinterpret_cast<float*>(stage_ptr(nk + (NW + wave) / C::STAGE_WAVES)) +
+                     ((NW + wave) % C::STAGE_WAVES) * C::MX_STAGE_FLOATS;
         static_for<0, TM>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
           const int r0 = m0 + wm * C::WTM + 32 * i;
-          static_for<0, TN>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
+          static_for<0, TN / 2>([&](auto jc) {
+            constexpr int j = 2 * decltype(jc)::value;
             const int cb = n0 + wn * C::WTN + 32 * j;
             if (cb < p.N) {
               float o[16];
 #pragma unroll
               for (int r = 0; r < 16; ++r) o[r] = acc[i][j][r];
               mx_stage(Wt, lane, o);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[r] = acc[i][j + 1][r];
+              mx_stage(Wt2, lane, o);
               wave_lds_sync();
-              mx_emit<typename EL::Fmt>(Wt, lane, p, r0, mlim, cb, 0, 0);
+              // a second block past N writes nothing: its rows start at mlim
+              mx_emit_two<typename EL::Fmt>(Wt, Wt2, lane, p, r0, cb + 32 < p.N ? r0 : mlim, cb,
+                                            cb + 32, 0, 0, mlim, 0);
               wave_lds_sync();
             }
           });
