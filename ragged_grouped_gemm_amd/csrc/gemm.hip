@@ -1551,12 +1551,12 @@ __global__ void __launch_bounds__(TL::WGM * TL::WGN * 64)
                   (wave % C::STAGE_WAVES) * C::MX_STAGE_FLOATS;
       // Two blocks are staged and quantized together (dGLU: the gate and the
       // linear block of a column block; GLU forward: the A blocks of row
-      // blocks 2 h and 2 h + 1); the second takes the next staging areas,
-      // which may reach into the last
-      // step's ring slot: every wave has finished reading it once all have
-      // passed this barrier (and no load is in flight after the last step)
-      // (for the GLU forward only with E4M3 codes: with E2M1 the pairing
-      // measured 21 % slower there, and 4 % faster for the dGLU)
+      // blocks 2 h and 2 h + 1).  The second takes the next staging areas,
+      // which may reach into the last step's ring slot: every wave has
+      // finished reading it once all have passed the barrier below, and no
+      // load is in flight after the last step.  For the GLU forward only
+      // with E4M3 codes: with E2M1 the pairing measured 21 % slower there
+      // (and 4 % faster for the dGLU).
       constexpr bool kPair = epi_glu_bwd(EPI) || EL::Fmt::WORDS == 8;
       float* Wt2 = nullptr;
       if constexpr (kPair) {
