@@ -237,7 +237,13 @@ def test_mx4_gemm_wgrad(counts, N, K):
     _, gc = ops.moe_mx_quantize_experts(gd, doff, dpad, R, want_row=False, fmt="e2m1")
     _, ac = ops.moe_mx_quantize_experts(ad, doff, dpad, R, want_row=False, fmt="e2m1")
     dw = ops.moe_grouped_gemm_bwd(gc, doff, mode="wgrad", a=ac, E=E, R=R, pad_offsets=dpad)
+    # accumulating onto zeros takes the direct float32 stores, the plain call
+    # the whole rows staged through LDS (over two ring slots): the same values
+    dw0 = torch.zeros_like(dw)
+    ops.moe_grouped_gemm_bwd(gc, doff, mode="wgrad", a=ac, E=E, R=R, pad_offsets=dpad, out=dw0,
+                             accumulate=True)
     torch.cuda.synchronize()
+    assert torch.equal(dw, dw0)
     Gc, Ac = deq4(gc), deq4(ac)
     got = host(dw)
     for e in range(E):

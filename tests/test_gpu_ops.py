@@ -375,7 +375,12 @@ def test_gemm_wgrad(dtype, counts, N, K):
     # accumulate: a second call adds to the first result, bias gradient included
     dw2, db2 = dw.clone(), db.clone()
     ops.moe_grouped_gemm_bwd(gd, offd, mode="wgrad", a=ad, out=dw2, db=db2, accumulate=True)
+    # accumulating onto zeros takes the direct float32 stores; the first call
+    # (big bf16 tiles) stores whole rows through LDS: the same values
+    dw3 = torch.zeros_like(dw)
+    ops.moe_grouped_gemm_bwd(gd, offd, mode="wgrad", a=ad, out=dw3, accumulate=True)
     torch.cuda.synchronize()
+    assert torch.equal(dw, dw3)
     ref, refb = om.grouped_wgrad(gh, ah, off, with_bias=True)
     got = host(dw)
     assert f32_ok(got, ref)
