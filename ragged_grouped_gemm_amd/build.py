@@ -7,7 +7,7 @@ Packed-fp32 instruction forms are disabled for all device code.
 
 --tuning builds ``libmoe_mi355x_tuning.so`` instead, with -DMOE_GEMM_TUNING:
 that library reads the grouped GEMM's tuning variables (MOE_GEMM_TILE,
-MOE_GEMM_GM, MOE_GEMM_SNAKE, MOE_GEMM_WGRAD, MOE_GEMM_GLU_DIRECT) from the environment, for sweeps; the product
+MOE_GEMM_GM, MOE_GEMM_GM_K, MOE_GEMM_SNAKE, MOE_GEMM_WGRAD, MOE_GEMM_GLU_DIRECT) from the environment, for sweeps; the product
 library never does.
 """
 from __future__ import annotations
