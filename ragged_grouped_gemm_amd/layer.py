@@ -28,7 +28,8 @@ the dgrads gain in proportion to R d f, so by default (``None``) they are
 made when the layer averages at least ``TRANSPOSE_MIN_ROWS`` routed rows per
 expert: measured at 4096 rows per expert (16384 tokens, top-8 of 32) both
 pay (step -1.5 ms), at 1024 (8192 tokens, top-4 of 32) neither does (step
-7.30 ms with both, 7.06 ms without).
+6.93-7.00 ms with both, 6.75 ms without; W2's copy alone breaks even, W1p's
+alone costs 0.2 ms).
 
 Activation recomputation (``recompute=True``): the forward does not write
 the pre-activation H; the backward first runs FC1 + GLU again (from x or Xp,
