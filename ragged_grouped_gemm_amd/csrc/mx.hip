@@ -112,8 +112,9 @@ __global__ void __launch_bounds__(256)
 // rows) into LDS, row stride TILE_LD elements (bf16: 528 bytes, fp32: 1040,
 // both 16 mod 256, so the 32 rows of a block read sit in distinct banks); the
 // gate product is applied as values leave LDS.  Thread t then quantizes row
-// t % 32 of 32-column block t / 32 into the row copy and column t over the 32
-// rows into the column copy.  Staging the input type rather than float32
+// t / 8 of 32-column block t % 8 into the row copy (so eight adjacent lanes
+// write one row's 256 columns contiguously) and column t over the 32 rows into
+// the column copy.  Staging the input type rather than float32
 // halves the LDS of a bf16 workgroup, which doubles the workgroups a compute
 // unit holds and so the loads in flight.
 template <class S>
@@ -190,9 +191,9 @@ __global__ void __launch_bounds__(256)
     __syncthreads();
     float v[32];
     uint32_t w8[8];
-    // row copy: row t % 32, block t / 32
+    // row copy: row t / 8, block t % 8 (eight lanes write a row's 256 columns)
     {
-      const int i = tid & 31, b = tid >> 5, col = c0 + 32 * b;
+      const int i = tid >> 3, b = tid & 7, col = c0 + 32 * b;
       const int r = s_row[i];
       if (rcodes && r >= 0 && col < n) {
         const float wi = s_w[i];
