@@ -181,12 +181,14 @@ def _routing(T, E, k, seed, empty=(1,)):
     return idx, w, offsets, pad, row_map, src_row
 
 
+@pytest.mark.parametrize("n", [256, 352])
 @pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_quantize_experts_bitexact(gated, dtype):
-    """Row and segment-column copies of x[src_row] (* gate), straight from x."""
-    note(f"mx quantize experts gated={gated} {dtype}")
-    T, E, k, n = 300, 6, 2, 256
+def test_quantize_experts_bitexact(gated, dtype, n):
+    """Row and segment-column copies of x[src_row] (* gate), straight from x;
+    n = 352 leaves the second 256-column chunk three blocks wide."""
+    note(f"mx quantize experts gated={gated} {dtype} n={n}")
+    T, E, k = 300, 6, 2
     idx, w, offsets, pad, row_map, src_row = _routing(T, E, k, 5)
     rng = np.random.default_rng(7)
     x64, xd = wide_values(rng, T, n, dtype)
